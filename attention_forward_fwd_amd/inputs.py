@@ -1,0 +1,126 @@
+"""Seeded synthetic inputs for the attention forward workloads.
+
+This module holds no attention arithmetic: it only draws random tensors (and zeroes whole
+mask words or rows for the structured variants).  The HIP path and the CPU oracle both take
+their inputs from here, on the CPU, so both see bit-identical values.
+
+Workloads follow the prefill grid of https://yetianai.com/news/16520 (section
+"七天跑出的成绩单": head dim 128, bf16, 32768 tokens split over batch x sequence length
+for S in {4096, 8192, 16384, 32768}, MHA with 16 heads, causal and non-causal, GQA with
+32 query heads over 4 or 8 KV heads) and the short random-mask case of
+https://yunpan.plus/t/19526-1-1 (section introduction: random per-(query, key) masks,
+context below 1k).  The pages give no value distribution; Q, K, V ~ N(0, 1) stands in.
+"""
+
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+
+import torch
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    dtype: str            # "bf16" | "f16"
+    mode: str             # "none" | "causal" | "bitmask"
+    batch: int
+    seq_len: int
+    n_q_heads: int
+    n_kv_heads: int
+    head_dim: int
+    seed: int
+    keep_prob: float = 0.5  # bitmask only; 0.5 draws every bit independently and uniformly
+    extra: dict = field(default_factory=dict, compare=False)
+
+    @property
+    def scale(self) -> float:
+        return self.head_dim ** -0.5
+
+    @property
+    def label(self) -> str:
+        return (f"{self.name}:{self.mode}:{self.dtype}:B{self.batch}xS{self.seq_len}:"
+                f"H{self.n_q_heads}/{self.n_kv_heads}:d{self.head_dim}")
+
+
+TORCH_DTYPE = {"bf16": torch.bfloat16, "f16": torch.float16}
+
+
+def mask_words(seq_len: int) -> int:
+    return (seq_len + 31) // 32
+
+
+def make_qkv(w: Workload):
+    """Q [B,S,Hq,D], K and V [B,S,Hkv,D] on the CPU, drawn as fp32 N(0,1) then rounded."""
+    g = torch.Generator(device="cpu").manual_seed(w.seed)
+    dt = TORCH_DTYPE[w.dtype]
+    q = torch.randn((w.batch, w.seq_len, w.n_q_heads, w.head_dim), generator=g).to(dt)
+    k = torch.randn((w.batch, w.seq_len, w.n_kv_heads, w.head_dim), generator=g).to(dt)
+    v = torch.randn((w.batch, w.seq_len, w.n_kv_heads, w.head_dim), generator=g).to(dt)
+    return q, k, v
+
+
+def make_bitmask(w: Workload, seed_offset: int = 7):
+    """Random packed mask [B, Hq, S, ceil(S/32)] as int32 words (uint32 bit patterns).
+
+    With keep_prob 0.5 every bit, padding bits past S included, is an independent fair coin:
+    a uniformly random 32-bit word.  Other keep probabilities draw one Bernoulli byte per bit
+    position and assemble words without any attention-specific arithmetic."""
+    g = torch.Generator(device="cpu").manual_seed(w.seed * 1009 + seed_offset)
+    shape = (w.batch, w.n_q_heads, w.seq_len, mask_words(w.seq_len))
+    if w.keep_prob == 0.5:
+        words = torch.randint(0, 2 ** 32, shape, generator=g, dtype=torch.int64)
+    else:
+        bits = (torch.rand(shape + (32,), generator=g) < w.keep_prob).to(torch.int64)
+        words = (bits * (2 ** torch.arange(32, dtype=torch.int64))).sum(-1)
+    return words.to(torch.uint32).view(torch.int32)
+
+
+def empty_rows(mask: torch.Tensor, rows) -> torch.Tensor:
+    """Copy of `mask` with the given query rows fully masked (all words zero) in every head."""
+    m = mask.clone()
+    m[:, :, list(rows), :] = 0
+    return m
+
+
+def empty_tiles(mask: torch.Tensor, tile: int, prob: float, seed: int) -> torch.Tensor:
+    """Copy of `mask` in which random whole (tile x tile) query/key blocks are cleared.
+
+    tile must be a multiple of 32 so a block covers whole words."""
+    assert tile % 32 == 0
+    B, H, S, W = mask.shape
+    g = torch.Generator(device="cpu").manual_seed(seed)
+    nb = (S + tile - 1) // tile
+    wpt = tile // 32
+    clear = torch.rand((B, H, nb, nb), generator=g) < prob
+    m = mask.clone()
+    for b, h, qi, kj in clear.nonzero().tolist():
+        m[b, h, qi * tile:(qi + 1) * tile, kj * wpt:(kj + 1) * wpt] = 0
+    return m
+
+
+# The benchmark grid.  Seed = 1000 * config + variant.
+def tiny_masked() -> Workload:
+    return Workload("tiny-masked", "f16", "bitmask", 1, 128, 1, 1, 64, seed=1000)
+
+
+def short_masked(seq_len: int = 512) -> Workload:
+    return Workload("short-masked", "f16", "bitmask", 16, seq_len, 16, 16, 64,
+                    seed=2000 + (0 if seq_len == 512 else 1))
+
+
+PREFILL_SHAPES = ((8, 4096), (4, 8192), (2, 16384), (1, 32768))
+
+
+def mha_prefill(batch: int, seq_len: int, causal: bool) -> Workload:
+    cfg = 4 if causal else 3
+    variant = [s for _, s in PREFILL_SHAPES].index(seq_len)
+    return Workload("mha-prefill", "bf16", "causal" if causal else "none", batch, seq_len,
+                    16, 16, 128, seed=1000 * cfg + variant)
+
+
+def gqa_prefill(batch: int, seq_len: int, n_kv_heads: int, causal: bool) -> Workload:
+    variant = [s for _, s in PREFILL_SHAPES].index(seq_len) + (0 if n_kv_heads == 4 else 4) \
+        + (8 if causal else 0)
+    return Workload("gqa-prefill", "bf16", "causal" if causal else "none", batch, seq_len,
+                    32, n_kv_heads, 128, seed=5000 + variant)
