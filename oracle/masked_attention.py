@@ -83,12 +83,12 @@ def kv_head_index(h: int, n_q_heads: int, n_kv_heads: int) -> int:
 
 
 def bit_of(words_row: np.ndarray, seq_len: int) -> np.ndarray:
-    """Unpack one mask row (W uint32 words) into a bool per key j < seq_len.
+    """Unpack mask words [..., W] (uint32) into a bool per key j < seq_len: [..., seq_len].
 
     Key j lives in word j // 32 at bit j % 32, least significant bit first; a set bit keeps.
     Bits for keys at or beyond seq_len are dropped."""
     j = np.arange(seq_len)
-    return ((words_row[j >> 5] >> (j & 31).astype(np.uint32)) & np.uint32(1)).astype(bool)
+    return ((words_row[..., j >> 5] >> (j & 31).astype(np.uint32)) & np.uint32(1)).astype(bool)
 
 
 def keep_rows(mode: str, rows: np.ndarray, seq_len: int, mask_rows=None) -> np.ndarray:
@@ -100,7 +100,7 @@ def keep_rows(mode: str, rows: np.ndarray, seq_len: int, mask_rows=None) -> np.n
     if mode == "causal":
         return np.arange(seq_len)[None, :] <= np.asarray(rows)[:, None]
     if mode == "bitmask":
-        return np.stack([bit_of(mask_rows[r], seq_len) for r in range(len(rows))])
+        return bit_of(np.asarray(mask_rows), seq_len)
     raise ValueError(f"unknown mode {mode!r}")
 
 

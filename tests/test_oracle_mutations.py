@@ -18,7 +18,7 @@ def _wrong_kv_head(h, n_q_heads, n_kv_heads):
 
 def _msb_first_bits(words_row, seq_len):
     j = np.arange(seq_len)
-    return ((words_row[j >> 5] >> (31 - (j & 31)).astype(np.uint32)) & np.uint32(1)).astype(bool)
+    return ((words_row[..., j >> 5] >> (31 - (j & 31)).astype(np.uint32)) & np.uint32(1)).astype(bool)
 
 
 def _inverted_polarity(words_row, seq_len):
@@ -27,10 +27,10 @@ def _inverted_polarity(words_row, seq_len):
 
 def _padding_kept(words_row, seq_len):
     # reads the bits past seq_len as if they were keys (then truncates wrongly)
-    W = len(words_row)
+    W = words_row.shape[-1]
     j = np.arange(W * 32)
-    bits = ((words_row[j >> 5] >> (j & 31).astype(np.uint32)) & np.uint32(1)).astype(bool)
-    return np.roll(bits, -(W * 32 - seq_len))[:seq_len]
+    bits = ((words_row[..., j >> 5] >> (j & 31).astype(np.uint32)) & np.uint32(1)).astype(bool)
+    return np.roll(bits, -(W * 32 - seq_len), axis=-1)[..., :seq_len]
 
 
 def _strict_causal(mode, rows, seq_len, mask_rows=None):
