@@ -1,0 +1,114 @@
+"""Thin Python binding of libfa.so (include/fa.h): argument marshalling only.
+
+Every step of the attention forward runs in the HIP kernels of libfa.so; PyTorch supplies
+device memory and the current HIP stream.  There is no CPU fallback: if the library is not
+built, or the tensors are not on a GPU, the call raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
+
+FA_MASK_NONE, FA_MASK_CAUSAL, FA_MASK_BITMASK = 0, 1, 2
+FA_DTYPE_F16, FA_DTYPE_BF16 = 0, 1
+MODES = {"none": FA_MASK_NONE, "causal": FA_MASK_CAUSAL, "bitmask": FA_MASK_BITMASK}
+DTYPES = {torch.float16: FA_DTYPE_F16, torch.bfloat16: FA_DTYPE_BF16}
+STATUS = {0: "FA_OK", 1: "FA_ERR_NULL_PTR", 2: "FA_ERR_BAD_SHAPE", 3: "FA_ERR_UNSUPPORTED",
+          4: "FA_ERR_BAD_MASK_MODE", 5: "FA_ERR_BAD_SCALE", 6: "FA_ERR_HIP"}
+EXPORTS = ("fa_fwd", "fa_status_string", "fa_abi_version")
+
+_lib = None
+
+
+class FaError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"{STATUS.get(status, status)}: {msg}")
+        self.status = status
+
+
+def lib_path() -> str:
+    return _LIB_PATH
+
+
+def load() -> ctypes.CDLL:
+    """Load libfa.so (built in-tree by attention_forward_fwd_amd.build); raises if missing."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            raise ImportError(f"{_LIB_PATH} is not built; run `python -m attention_forward_fwd_amd.build`")
+        lib = ctypes.CDLL(_LIB_PATH)
+        lib.fa_fwd.restype = ctypes.c_int
+        lib.fa_fwd.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                               ctypes.c_int, ctypes.c_int, ctypes.c_float, ctypes.c_void_p,
+                               ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                               ctypes.c_void_p]
+        lib.fa_status_string.restype = ctypes.c_char_p
+        lib.fa_status_string.argtypes = [ctypes.c_int]
+        lib.fa_abi_version.restype = ctypes.c_int
+        lib.fa_abi_version.argtypes = []
+        _lib = lib
+    return _lib
+
+
+def fa_status_string(status: int) -> str:
+    return load().fa_status_string(int(status)).decode()
+
+
+def fa_fwd_raw(dtype: int, mask_mode: int, batch: int, n_q_heads: int, n_kv_heads: int,
+               seq_len: int, head_dim: int, scale: float, q: int, k: int, v: int, mask: int,
+               o: int, stream: int) -> int:
+    """Direct call of the C entry point with integer pointers; returns the fa_status code."""
+    return load().fa_fwd(dtype, mask_mode, batch, n_q_heads, n_kv_heads, seq_len, head_dim,
+                         ctypes.c_float(scale), q, k, v, mask, o, stream)
+
+
+def fa_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, mode: str = "none",
+           scale: float | None = None, mask: torch.Tensor | None = None,
+           out: torch.Tensor | None = None) -> torch.Tensor:
+    """O = softmax(scale Q K^T + mask) V on the GPU (see include/fa.h for the definition).
+
+    q [B,S,Hq,D], k/v [B,S,Hkv,D] (bf16 or fp16, contiguous, on one GPU); mask [B,Hq,S,ceil(S/32)]
+    int32/uint32 words for mode "bitmask".  Enqueued on torch's current stream; returns o."""
+    if mode not in MODES:
+        raise ValueError(f"mode must be one of {sorted(MODES)}")
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a GPU tensor (there is no CPU path)")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+        if t.dim() != 4:
+            raise ValueError(f"{name} must be 4-D [B, S, H, D]")
+    if q.dtype not in DTYPES or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("q, k, v must share dtype bfloat16 or float16")
+    B, S, Hq, D = q.shape
+    if k.shape != v.shape or k.shape[0] != B or k.shape[1] != S or k.shape[3] != D:
+        raise ValueError("k and v must be [B, S, Hkv, D] matching q")
+    Hkv = k.shape[2]
+    if scale is None:
+        scale = D ** -0.5
+    mptr = 0
+    if mode == "bitmask":
+        W = (S + 31) // 32
+        if mask is None or tuple(mask.shape) != (B, Hq, S, W):
+            raise ValueError(f"bitmask mode needs mask of shape {(B, Hq, S, W)}")
+        if mask.dtype not in (torch.int32, getattr(torch, "uint32", torch.int32)):
+            raise ValueError("mask must hold 32-bit words")
+        if not mask.is_cuda or not mask.is_contiguous():
+            raise ValueError("mask must be a contiguous GPU tensor")
+        mptr = mask.data_ptr()
+    if out is None:
+        out = torch.empty_like(q)
+    elif out.shape != q.shape or out.dtype != q.dtype or not out.is_contiguous():
+        raise ValueError("out must be a contiguous tensor like q")
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    with torch.cuda.device(q.device):
+        st = fa_fwd_raw(DTYPES[q.dtype], MODES[mode], B, Hq, Hkv, S, D, float(scale),
+                        q.data_ptr(), k.data_ptr(), v.data_ptr(), mptr, out.data_ptr(), stream)
+    if st != 0:
+        raise FaError(st, fa_status_string(st))
+    return out

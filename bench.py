@@ -1,0 +1,169 @@
+#!/usr/bin/env python3
+"""Benchmark of the FlashAttention forward (libfa.so) on one MI355X.
+
+One step = one fa_fwd launch over the whole workload (every row tile, every head and
+batch), inputs already resident in device memory.  Default workload: non-causal MHA prefill,
+bf16, head dim 128, 16 heads, batch 4 x 8192 tokens (the 32768-token prefill grid of
+https://yetianai.com/news/16520, section "七天跑出的成绩单").  The causal variant of the same
+shape is timed alongside and reported under "also".
+
+Prints ONE JSON line.  FLOPs are counted dense, 4*B*Hq*S^2*d, half of that for causal.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "attn fwd TFLOP/s + % of MI355X bf16 MFMA peak (hdim128, causal/non-causal)"
+PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA: 256 CU x 2.4 GHz x 4096 FLOP/clk
+PEAK_HBM_GBS = 8000.0
+
+
+def flops(B, H, S, D, mode):
+    f = 4.0 * B * H * S * S * D
+    return f / 2 if mode == "causal" else f
+
+
+def time_launches(fn, steps, warmup):
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(steps):
+        fn()
+    end.record(stream)
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / steps   # ms per launch, HIP events on the launch stream
+
+
+def cpu_baseline(w, q, k, v, o_gpu, budget_s):
+    """Time the fp64 oracle on a bounded sample of the same workload (row blocks of one head
+    at full key length, as many as fit in budget_s) and check the GPU rows it covers."""
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [os.cpu_count()])
+    except Exception:
+        cores = os.cpu_count()
+    S, H = w.seq_len, w.n_q_heads
+    rng = np.random.default_rng(w.seed)
+    done_rows, t_used, max_err, sum_err, n_el = 0, 0.0, 0.0, 0.0, 0
+    blocks = []
+    while t_used < budget_s and len(blocks) < 64:
+        b, h = int(rng.integers(0, w.batch)), int(rng.integers(0, H))
+        r0 = int(rng.integers(0, max(1, S - 256)))
+        rows = np.arange(r0, min(S, r0 + 256))
+        t0 = time.perf_counter()
+        ref = oracle.attention_rows(q, k, v, w.mode, w.scale, None, rows=rows, heads=[h],
+                                    batches=[b])
+        t_used += time.perf_counter() - t0
+        got = o_gpu[b, rows[0]:rows[-1] + 1, h].float().cpu().numpy().astype(np.float64)
+        err = np.abs(got - ref[0, :, 0, :])
+        max_err = max(max_err, float(err.max()))
+        sum_err += float(err.sum())
+        n_el += err.size
+        done_rows += len(rows)
+        blocks.append((b, h, int(rows[0])))
+    per_row = 4.0 * S * w.head_dim * (0.5 if w.mode == "causal" else 1.0)
+    tflops = done_rows * per_row / t_used / 1e12
+    return {
+        "value": tflops, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+        "sample": f"{done_rows} query rows ({len(blocks)} blocks of 256 rows, one head each) at "
+                  f"full key length {S}, fp64 numpy, {t_used:.1f} s; dense-equivalent FLOPs",
+        "gpu_vs_oracle_on_sample": {"max_abs": max_err, "mean_abs": sum_err / max(1, n_el)},
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--batch", type=int, default=4)
+    ap.add_argument("--seq-len", type=int, default=8192)
+    ap.add_argument("--cpu-budget", type=float, default=12.0,
+                    help="seconds of oracle work for the CPU baseline (0 = skip)")
+    ap.add_argument("--no-also", action="store_true", help="skip the causal companion timing")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              f"(the forward shards over independent (batch, KV head) groups with no "
+              f"communication, so aggregate throughput is N x the one-GPU value).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from attention_forward_fwd_amd import fa_fwd, inputs
+
+    dev = torch.device("cuda:0")
+    w = inputs.mha_prefill(args.batch, args.seq_len, causal=False)
+    q, k, v = inputs.make_qkv(w)
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    out = torch.empty_like(qd)
+
+    def step(mode=w.mode):
+        fa_fwd(qd, kd, vd, mode=mode, scale=w.scale, out=out)
+
+    ms = time_launches(step, args.steps, args.warmup)
+    f = flops(w.batch, w.n_q_heads, w.seq_len, w.head_dim, w.mode)
+    tflops = f / (ms * 1e-3) / 1e12
+    o_main = out.clone()
+
+    also = {}
+    if not args.no_also:
+        ms_c = time_launches(lambda: step("causal"), max(5, args.steps // 2), 3)
+        fc = flops(w.batch, w.n_q_heads, w.seq_len, w.head_dim, "causal")
+        also[f"causal B{w.batch} S{w.seq_len}"] = {
+            "tflops": fc / (ms_c * 1e-3) / 1e12, "ms": ms_c,
+            "frac_of_peak": fc / (ms_c * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
+
+    bytes_alg = 4 * w.batch * w.seq_len * w.n_q_heads * w.head_dim * 2   # Q, K, V read + O written
+    traffic = None
+    tfile = os.path.join(ROOT, "profiles", "traffic.json")
+    if os.path.exists(tfile):
+        try:
+            tr = json.load(open(tfile))
+            key = f"{w.mode}:B{w.batch}:S{w.seq_len}:H{w.n_q_heads}:d{w.head_dim}"
+            traffic = tr.get(key)
+        except Exception:
+            traffic = None
+    rec = {
+        "metric": METRIC,
+        "value": tflops,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"non-causal MHA prefill bf16 d128 H16 B{w.batch} S{w.seq_len}",
+                   "batch": w.batch, "seq_len": w.seq_len, "n_q_heads": w.n_q_heads,
+                   "n_kv_heads": w.n_kv_heads, "head_dim": w.head_dim, "mask_mode": w.mode},
+        "roofline": {"bound": "mfma", "achieved": tflops, "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": tflops / PEAK_BF16_TFLOPS, "traffic": traffic,
+                     "algorithmic_bytes": bytes_alg,
+                     "kernel": "fa_fwd_kernel<bf16, d128, none>"},
+        "also": also,
+    }
+    if args.cpu_budget > 0:
+        rec["cpu_baseline"] = cpu_baseline(w, q, k, v, o_main, args.cpu_budget)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

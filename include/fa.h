@@ -1,0 +1,89 @@
+/*
+ * fa.h -- C ABI of libfa.so, a FlashAttention forward pass for AMD MI355X (gfx950).
+ *
+ * Operation (fa_fwd):  O = softmax(scale * Q K^T + mask) V, per batch and query head, computed
+ * tile by tile with a running (online) softmax so the S x S score matrix never reaches device
+ * memory.  Pages this follows:
+ *   - https://yetianai.com/news/16520, section "传统进化搜索的天花板": FlashAttention computes
+ *     attention block-wise without storing the full attention matrix; FA4's correction step
+ *     rescales the accumulator of the single-pass softmax.  Section "七天跑出的成绩单": forward
+ *     prefill at head dim 128 in bf16, causal and non-causal, MHA and GQA (32 query heads over 4
+ *     or 8 KV heads).
+ *   - https://yunpan.plus/t/19526-1-1, section "AI生成的代码质量如何？", excerpt 2: the custom
+ *     mask is one bit per (query row, key); key j is bit j % 32 of word j / 32 (least significant
+ *     bit first); a set bit keeps the score; rows and keys at or beyond seq_len are never kept.
+ *
+ * Result definition, for batch b, query head h, query row i < S, with G = n_q_heads/n_kv_heads
+ * and KV head g = h / G (each run of G consecutive query heads shares one KV head):
+ *     s_j  = scale * <Q[b,i,h,:], K[b,j,g,:]>                 for keys j < S
+ *     kept = none: every j;  causal: j <= i;  bitmask: bit (j % 32) of mask[b,h,i,j/32]
+ *     O[b,i,h,:] = sum_j softmax over kept j (s_j) * V[b,j,g,:];   O = 0 when no key is kept.
+ *
+ * Layouts (row-major, contiguous, element strides implied by the shapes):
+ *     q, o  [batch, seq_len, n_q_heads,  head_dim]   dtype elements (2 bytes)
+ *     k, v  [batch, seq_len, n_kv_heads, head_dim]   dtype elements
+ *     mask  [batch, n_q_heads, seq_len, W] uint32, W = ceil(seq_len / 32); bits for keys >= S
+ *           are ignored.  Only read in FA_MASK_BITMASK mode.
+ *
+ * Numerics: Q K^T and P V run on bf16/fp16 matrix cores with fp32 accumulation; softmax runs in
+ * fp32 (exp2 with log2(e) folded into the scale); P is rounded to the input dtype before P V;
+ * O is rounded to the input dtype (round to nearest even).  A negative scale is handled exactly
+ * (the sign is moved onto Q).  Inputs must be finite and |scale * s_j| must stay below 1e30.
+ * Results are bitwise deterministic for a given input and device.
+ *
+ * Ownership and threading: every pointer is a DEVICE pointer owned by the caller, 16-byte
+ * aligned (mask: 4-byte aligned).  The library allocates nothing, keeps no state, never
+ * synchronises, and enqueues one kernel on `stream` (a hipStream_t; NULL = default stream).
+ * o must not alias q, k, v or mask.  Calls are safe from several host threads.
+ *
+ * Errors: arguments are validated first, synchronously, with no HIP call; on error nothing is
+ * enqueued and o is untouched.  After the launch, a launch error reported by HIP returns
+ * FA_ERR_HIP.  Faults during execution surface at the caller's next synchronisation, as for any
+ * HIP kernel.  Nothing is printed and no C++ exception crosses this interface.
+ */
+#ifndef FA_H_
+#define FA_H_
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FA_ABI_VERSION 1
+
+typedef enum {
+  FA_MASK_NONE = 0,     /* every key kept */
+  FA_MASK_CAUSAL = 1,   /* key j kept for query i iff j <= i (diagonal kept) */
+  FA_MASK_BITMASK = 2   /* packed per-(query, key) bits, 1 = keep */
+} fa_mask_mode;
+
+typedef enum { FA_DTYPE_F16 = 0, FA_DTYPE_BF16 = 1 } fa_dtype;
+
+typedef enum {
+  FA_OK = 0,
+  FA_ERR_NULL_PTR = 1,      /* q, k, v or o is NULL */
+  FA_ERR_BAD_SHAPE = 2,     /* batch, seq_len or a head count <= 0, n_q_heads % n_kv_heads != 0,
+                               or a tensor larger than 2^31 elements per batch */
+  FA_ERR_UNSUPPORTED = 3,   /* head_dim not 64 or 128, unknown dtype, misaligned pointer */
+  FA_ERR_BAD_MASK_MODE = 4, /* unknown mask_mode, or FA_MASK_BITMASK with mask == NULL */
+  FA_ERR_BAD_SCALE = 5,     /* scale is NaN or infinite */
+  FA_ERR_HIP = 6            /* the HIP runtime rejected the launch */
+} fa_status;
+
+/* Forward attention (see the definition above).  Returns FA_OK once the kernel is enqueued. */
+fa_status fa_fwd(fa_dtype dtype, fa_mask_mode mask_mode, int batch, int n_q_heads,
+                 int n_kv_heads, int seq_len, int head_dim, float scale, const void* q,
+                 const void* k, const void* v, const uint32_t* mask, void* o, void* stream);
+
+/* Static, NUL-terminated description of a status code (never NULL). */
+const char* fa_status_string(int status);
+
+/* FA_ABI_VERSION of the loaded library. */
+int fa_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H_ */

@@ -1,0 +1,94 @@
+"""C-ABI checks that need no GPU: the library loads, exports what include/fa.h declares,
+validates arguments before touching the device, and links no vendor math library."""
+
+import os
+import re
+import subprocess
+
+import pytest
+
+import attention_forward_fwd_amd as fa
+from attention_forward_fwd_amd import fa as fab
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa.h")
+
+
+def _lib():
+    if not os.path.exists(fa.lib_path()):
+        pytest.skip("libfa.so not built (run __graft_entry__.build())")
+    return fa.load()
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\*?(fa_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_entry_points():
+    assert _declared_functions() == sorted(fab.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    _lib()
+    out = subprocess.run(["nm", "-D", "--defined-only", fa.lib_path()], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if line.strip()}
+    for name in _declared_functions():
+        assert name in exported, f"{name} declared in fa.h but not exported"
+
+
+def test_no_vendor_math_library_linked():
+    _lib()
+    out = subprocess.run(["readelf", "-d", fa.lib_path()], capture_output=True, text=True,
+                         check=True).stdout
+    needed = re.findall(r"\(NEEDED\).*\[(.+?)\]", out)
+    banned = ("rocblas", "hipblas", "miopen", "composable", "ck_", "rocwmma", "triton", "torch")
+    assert not [n for n in needed if any(b in n.lower() for b in banned)], needed
+    undef = subprocess.run(["nm", "-D", "--undefined-only", fa.lib_path()], capture_output=True,
+                           text=True, check=True).stdout.lower()
+    assert not any(b in undef for b in ("rocblas", "hipblas", "miopen")), "vendor GEMM symbols"
+
+
+def test_abi_version_and_status_strings():
+    lib = _lib()
+    assert lib.fa_abi_version() == 1
+    for code, name in fab.STATUS.items():
+        s = fa.fa_status_string(code)
+        assert s and isinstance(s, str)
+    assert fa.fa_status_string(12345) == "unknown status"
+
+
+# Arguments that must be rejected synchronously, before any HIP call (no GPU is touched, so
+# these run on a CPU-only machine).  Fake but 16-byte-aligned pointers are never dereferenced.
+P = 0x10000
+
+
+def _call(**kw):
+    a = dict(dtype=1, mode=0, B=1, Hq=2, Hkv=1, S=8, D=128, scale=0.1, q=P, k=P, v=P, mask=0,
+             o=P, stream=0)
+    a.update(kw)
+    return fa.fa_fwd_raw(a["dtype"], a["mode"], a["B"], a["Hq"], a["Hkv"], a["S"], a["D"],
+                         a["scale"], a["q"], a["k"], a["v"], a["mask"], a["o"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=0), 1), (dict(k=0), 1), (dict(v=0), 1), (dict(o=0), 1),
+    (dict(B=0), 2), (dict(S=0), 2), (dict(S=-5), 2), (dict(Hq=0), 2), (dict(Hkv=0), 2),
+    (dict(Hq=6, Hkv=4), 2), (dict(S=1 << 20, Hq=128, Hkv=1), 2),
+    (dict(D=96), 3), (dict(D=256), 3), (dict(dtype=7), 3), (dict(q=P + 8), 3), (dict(o=P + 2), 3),
+    (dict(mode=3), 4), (dict(mode=-1), 4), (dict(mode=2, mask=0), 4), (dict(mode=2, mask=P + 2), 4),
+    (dict(scale=float("nan")), 5), (dict(scale=float("inf")), 5), (dict(scale=float("-inf")), 5),
+])
+def test_invalid_arguments_rejected_before_launch(kw, status):
+    _lib()
+    assert _call(**kw) == status
+
+
+def test_python_binding_refuses_cpu_tensors():
+    import torch
+    _lib()
+    q = torch.zeros(1, 8, 2, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="GPU"):
+        fa.fa_fwd(q, q, q)

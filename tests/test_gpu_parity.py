@@ -1,0 +1,181 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 CPU oracle on seeded inputs.
+
+Bounds (max-abs / mean-abs): bf16 2e-2 / 2e-3, fp16 5e-3 / 5e-4.  Small and short-sequence
+workloads are compared on every output element; the long prefill workloads on sampled rows
+(all batches and heads, rows at tile edges, the ends, the middle and seeded random rows) at
+full key length, in the same launch configuration the benchmark times.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from attention_forward_fwd_amd import inputs
+from gpu_util import check_full, check_sampled, log, run_gpu, to64, compare
+import oracle
+
+pytestmark = pytest.mark.gpu
+
+
+def _qkv(B, S, Hq, Hkv, D, dtype, seed):
+    w = inputs.Workload("edge", dtype, "none", B, S, Hq, Hkv, D, seed=seed)
+    return inputs.make_qkv(w)
+
+
+def _mask(B, Hq, S, seed):
+    w = inputs.Workload("edge", "f16", "bitmask", B, S, Hq, Hq, 64, seed=seed)
+    return inputs.make_bitmask(w)
+
+
+# ----------------------------------------------------------------- the five workloads
+def test_tiny_masked():
+    w = inputs.tiny_masked()
+    q, k, v = inputs.make_qkv(w)
+    m = inputs.make_bitmask(w)
+    log(f"case {w.label}")
+    check_full(q, k, v, "bitmask", w.scale, m, w.label)
+    m2 = inputs.empty_rows(m, [0, 17, w.seq_len - 1])
+    _, o = check_full(q, k, v, "bitmask", w.scale, m2, w.label + " rows 0,17,S-1 empty")
+    assert (to64(o)[0, [0, 17, w.seq_len - 1]] == 0).all()
+
+
+@pytest.mark.parametrize("S", [512, 1000])
+def test_short_masked(S):
+    w = inputs.short_masked(S)
+    q, k, v = inputs.make_qkv(w)
+    m = inputs.make_bitmask(w)
+    log(f"case {w.label}")
+    check_full(q, k, v, "bitmask", w.scale, m, w.label)
+
+
+def test_short_masked_empty_tiles():
+    # Whole 64x64 blocks cleared: the wave ballot skips them; the result must not change.
+    w = inputs.short_masked(512)
+    q, k, v = inputs.make_qkv(w)
+    m = inputs.empty_tiles(inputs.make_bitmask(w), 64, 0.4, seed=w.seed + 50)
+    log(f"case {w.label} empty 64x64 tiles")
+    check_full(q, k, v, "bitmask", w.scale, m, w.label + " empty tiles")
+
+
+@pytest.mark.parametrize("causal", [False, True], ids=["noncausal", "causal"])
+@pytest.mark.parametrize("B,S", inputs.PREFILL_SHAPES, ids=lambda x: str(x))
+def test_mha_prefill(B, S, causal):
+    w = inputs.mha_prefill(B, S, causal)
+    q, k, v = inputs.make_qkv(w)
+    log(f"case {w.label}")
+    check_sampled(q, k, v, w.mode, w.scale, None, w.label, seed=w.seed)
+
+
+@pytest.mark.parametrize("causal", [False, True], ids=["noncausal", "causal"])
+@pytest.mark.parametrize("Hkv", [4, 8])
+@pytest.mark.parametrize("B,S", inputs.PREFILL_SHAPES, ids=lambda x: str(x))
+def test_gqa_prefill(B, S, Hkv, causal):
+    w = inputs.gqa_prefill(B, S, Hkv, causal)
+    q, k, v = inputs.make_qkv(w)
+    log(f"case {w.label}")
+    check_sampled(q, k, v, w.mode, w.scale, None, w.label, seed=w.seed)
+
+
+# ----------------------------------------------------------------- edge cases
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("mode", ["none", "causal", "bitmask"])
+@pytest.mark.parametrize("S", [1, 2, 31, 33, 64, 65, 127, 129, 200, 1000])
+def test_ragged_lengths(S, mode, D, dtype):
+    B, Hq, Hkv = 2, 6, 2   # group of 3: rows of one tile mix positions and heads unevenly
+    seed = 7000 + S * 7 + D + (1 if dtype == "f16" else 0)
+    q, k, v = _qkv(B, S, Hq, Hkv, D, dtype, seed)
+    m = _mask(B, Hq, S, seed) if mode == "bitmask" else None
+    label = f"ragged S={S} {mode} d={D} {dtype} B={B} H={Hq}/{Hkv}"
+    log(f"case {label}")
+    check_full(q, k, v, mode, D ** -0.5, m, label)
+
+
+@pytest.mark.parametrize("Hq,Hkv", [(8, 8), (8, 1), (32, 4), (12, 3), (5, 5)])
+@pytest.mark.parametrize("mode", ["none", "causal", "bitmask"])
+def test_head_groupings(Hq, Hkv, mode):
+    S, D = 300, 128
+    q, k, v = _qkv(1, S, Hq, Hkv, D, "bf16", 8000 + Hq * 10 + Hkv)
+    m = _mask(1, Hq, S, 8100 + Hq) if mode == "bitmask" else None
+    label = f"heads {Hq}/{Hkv} {mode} S={S}"
+    log(f"case {label}")
+    check_full(q, k, v, mode, D ** -0.5, m, label)
+
+
+@pytest.mark.parametrize("scale", [0.0, -0.125, 1.0, 2.5])
+@pytest.mark.parametrize("mode", ["none", "causal", "bitmask"])
+def test_scales(scale, mode):
+    S, D = 257, 64
+    q, k, v = _qkv(1, S, 4, 2, D, "f16", 9000)
+    m = _mask(1, 4, S, 9001) if mode == "bitmask" else None
+    label = f"scale={scale} {mode}"
+    log(f"case {label}")
+    check_full(q, k, v, mode, scale, m, label)
+
+
+def test_padding_bits_ignored():
+    S = 1000
+    q, k, v = _qkv(2, S, 4, 4, 64, "f16", 9100)
+    m = _mask(2, 4, S, 9101)
+    m_flip = m.clone()
+    m_flip[..., -1] = m_flip[..., -1] ^ torch.tensor(-(1 << (S % 32)), dtype=torch.int32)
+    a = run_gpu(q, k, v, "bitmask", 0.125, m)
+    b = run_gpu(q, k, v, "bitmask", 0.125, m_flip)
+    assert torch.equal(a, b), "bits for keys >= S changed the output"
+
+
+def test_single_kept_key_returns_value_row():
+    S, H, D = 150, 2, 128
+    q, k, v = _qkv(1, S, H, H, D, "bf16", 9200)
+    rng = np.random.default_rng(9201)
+    picks = rng.integers(0, S, size=(H, S))
+    words = np.zeros((1, H, S, (S + 31) // 32), dtype=np.uint32)
+    for h in range(H):
+        for i in range(S):
+            j = picks[h, i]
+            words[0, h, i, j // 32] = np.uint32(1) << np.uint32(j % 32)
+    m = torch.from_numpy(words.view(np.int32))
+    o = run_gpu(q, k, v, "bitmask", 0.3, m).cpu()
+    for h in range(H):
+        assert torch.equal(o[0, :, h], v[0, picks[h], h]), "one kept key must return V[j] exactly"
+
+
+def test_causal_equals_lower_triangular_bitmask():
+    S, H = 333, 4
+    q, k, v = _qkv(1, S, H, H, 128, "bf16", 9300)
+    tri = np.tril(np.ones((S, S), dtype=bool))
+    W = (S + 31) // 32
+    padded = np.zeros((S, W * 32), dtype=np.uint64)
+    padded[:, :S] = tri
+    words = (padded << (np.arange(W * 32) % 32).astype(np.uint64)).reshape(S, W, 32).sum(-1)
+    m = torch.from_numpy(np.broadcast_to(words.astype(np.uint32), (1, H, S, W)).copy().view(np.int32))
+    a = run_gpu(q, k, v, "causal", 0.1, None)
+    b = run_gpu(q, k, v, "bitmask", 0.1, m)
+    assert torch.equal(a, b), "causal must equal the lower-triangular bitmask bit for bit"
+
+
+def test_deterministic():
+    w = inputs.mha_prefill(8, 4096, True)
+    q, k, v = inputs.make_qkv(w)
+    dev = torch.device("cuda:0")
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    from attention_forward_fwd_amd import fa_fwd
+    a = fa_fwd(qd, kd, vd, mode="causal")
+    b = fa_fwd(qd, kd, vd, mode="causal")
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("S", [33, 1000])
+def test_no_out_of_bounds_writes(S):
+    B, Hq, Hkv, D = 1, 3, 1, 128
+    q, k, v = _qkv(B, S, Hq, Hkv, D, "bf16", 9400 + S)
+    n = q.numel()
+    pad = 4096
+    dev = torch.device("cuda:0")
+    buf = torch.full((n + 2 * pad,), 12345.0, dtype=torch.bfloat16, device=dev)
+    out = buf[pad:pad + n].view(q.shape)
+    run_gpu(q, k, v, "causal", D ** -0.5, None, out=out)
+    assert (buf[:pad] == 12345.0).all() and (buf[pad + n:] == 12345.0).all(), "guard band written"
+    want = oracle.attention(q, k, v, "causal", D ** -0.5)
+    compare(to64(out), want, q.dtype, f"guarded S={S}")
