@@ -28,10 +28,15 @@
 //     touches only the lane's own query.  P never leaves registers: the S^T accumulator layout
 //     is re-used directly as the B operand of the P V product (keys permuted consistently on
 //     both operands).
-//   * LDS: K tile [BN][D] and the Q staging tile with 16-byte chunks XOR-swizzled by row; V is
-//     written transposed ([D][BN]) with the key order permuted to match the P register layout,
-//     so every MFMA operand is one 128-bit ds_read.  K/V/mask tiles are double-buffered with
-//     one workgroup barrier per tile.
+//   * LDS: K and V tiles are copied global -> LDS by the DMA path (global_load_lds_dwordx4, no
+//     registers), row-major [BN][D] with 16-byte chunks XOR-swizzled by row; the swizzle is
+//     applied to the global addresses since the DMA writes LDS in lane order.  K operands are
+//     128-bit ds_reads; V operands come from ds_read_b64_tr_b16, which transposes 16-bit
+//     elements across each 16-lane group (lane j of the group receives element j%4 of lanes
+//     j/4 + 4t, t = 0..3), turning 4 key rows of V into the 4 keys one MFMA lane needs at its
+//     head_dim column.  K/V/mask tiles are double-buffered, one workgroup barrier per tile.
+//     Key rows past the sequence end are loaded from the last valid row (address clamp) and
+//     masked, so their probabilities are exactly 0.
 //   * Softmax: exp2 with log2(e) folded into the scale, running max floored at -1e30 so a
 //     fully masked row never makes NaN, unconditional (branch-free) rescale of O and l every
 //     tile, masked scores set to -inf with one bit-field extract and one bit-field insert.
@@ -76,11 +81,17 @@ struct Params {
   u32 qflip;  // 0x80008000 when scale < 0 (moves the sign onto Q exactly), else 0
 };
 
-// Tile shape shared by every instance.
+// Tile shape shared by every instance: 4 waves of 32 rows, 64 keys per tile; two workgroups
+// share a CU (two waves per SIMD, from different workgroups, so one wave's vector work can run
+// while the other's matrix work occupies the matrix cores).
 constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * 64;
 constexpr int kBM = kWaves * 32;  // rows per workgroup
 constexpr int kBN = 64;           // keys per tile
+#ifndef FA_PREFETCH
+#define FA_PREFETCH 1
+#endif
+constexpr int kPrefetch = FA_PREFETCH;  // matrix-phase operand steps read ahead
 
 template <bool BF16>
 __device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
@@ -108,6 +119,21 @@ __device__ __forceinline__ u32x2 pack4(f32x4 x) {
     return __builtin_bit_cast(u32x2, __builtin_convertvector(x, f16x4));
 }
 
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+// acc + x.lo + x.hi for a packed pair of 16-bit floats (v_dot2 against (1, 1)).
+template <bool BF16>
+__device__ __forceinline__ float dot2_ones(u32 x, float acc) {
+  if constexpr (BF16) {
+    const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, x), one, acc, false);
+  } else {
+    const f16x2 one = {(_Float16)1.0f, (_Float16)1.0f};
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, x), one, acc, false);
+  }
+}
+
 // Both lane halves (l and l^32) hold the same query: combine their partial values.
 __device__ __forceinline__ float max_halves(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
@@ -123,31 +149,80 @@ __device__ __forceinline__ u32 low_bits(int n) {
   return n >= 32 ? ~0u : (n <= 0 ? 0u : ((1u << n) - 1u));
 }
 
+// LDS layout of a K, V or Q tile (rows = keys or query rows, 16-byte chunks of head_dim).
+// A "region" is the 1 KiB one wave-wide DMA instruction writes (lane i -> byte 16 i): it holds
+// RPR whole rows (4 at d=128, 8 at d=64), chunk c of row rr at slot c*RPR + (rr ^ x(c)), and
+// regions are padded to a stride of RS bytes.  Why:
+//   * a DMA instruction reads RPR complete rows, 1 KiB contiguous per row group (coalesced);
+//   * every operand address is a per-lane base plus compile-time offsets for the k-step, the
+//     32-key block, the head_dim block and the buffer, so no per-read address registers;
+//   * with 64 banks x 4 B: the 128-bit operand reads (16 lanes, one chunk of 16 consecutive
+//     rows) and the transposing reads (32 lanes, 4 consecutive chunks of 4 consecutive rows)
+//     touch every bank at most once per 256 bytes.  The padding shifts consecutive regions by
+//     16 (d=128) or 32 (d=64) banks; at d=64 the row index is also XORed with bit 1 of the
+//     chunk (x(c) = 4 * ((c >> 1) & 1)), since a d=64 region spans two bank lines.
+template <int D>
+struct Lds {
+  static constexpr int RB = D * 2;              // bytes of one row's data
+  static constexpr int RPR = 1024 / RB;         // rows per region
+  static constexpr int RS = D == 128 ? 1088 : 1152;
+  static constexpr int KC = D / 8;              // chunks per row
+  __device__ static constexpr int x(int c) { return D == 64 ? 4 * ((c >> 1) & 1) : 0; }
+  // byte offset of (row r, chunk c) within a tile
+  __device__ static constexpr int off(int r, int c) {
+    return (r / RPR) * RS + (c * RPR + ((r % RPR) ^ x(c))) * 16;
+  }
+};
+
+// LDS layout of a transposed V tile: row d (one head_dim index) holds the BN = 64 keys of the
+// tile, 128 bytes, as 8 "units" of 16 bytes.  Unit u = 2ks + hl holds keys 16ks + 4hl + 0..3
+// (first 8 bytes) and 16ks + 8 + 4hl + 0..3 (last 8 bytes): exactly the 8 keys, in register
+// order, that lane half hl of an MFMA needs at k-step ks of P V, so each V^T operand is one
+// 128-bit read.  Row d lives in 256-byte line d/2, half h(d) = (d ^ d/4) & 1, with unit u at
+// slot u ^ f(d), f(d) = (d/2) & 7.  With 64 banks x 4 B, the operand reads (16 lanes, one unit
+// of 16 consecutive rows) and the staging writes (32 lanes, two whole rows d and d+4) touch
+// every bank once.  The read address is a per-lane base XOR 32*ks, plus 4096 per 32-row block.
+struct VtLds {
+  __device__ static constexpr int off(int d, int u, int half) {
+    return (d >> 1) * 256 + ((d ^ (d >> 2)) & 1) * 128 + ((u ^ ((d >> 1) & 7)) * 16) + half * 8;
+  }
+};
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+typedef __attribute__((address_space(3))) void lds_void;
+
 template <bool BF16, int D, int MODE>
 __global__ __launch_bounds__(kThreads, 2) void fa_fwd_kernel(Params p) {
-  constexpr int BM = kBM, BN = kBN, NT = kThreads;
-  constexpr int KC = D / 8;      // 16-byte chunks in a K/Q row
-  constexpr int VC = BN / 8;     // 16-byte chunks in a transposed-V row
-  constexpr int NKB = BN / 32;   // 32-key blocks per tile (one MFMA output block each)
-  constexpr int QKS = D / 16;    // MFMA k-steps of Q K^T
-  constexpr int NDB = D / 32;    // 32-wide blocks of head_dim in O
-  constexpr int PKS = BN / 16;   // MFMA k-steps of P V
-  constexpr int K_BYTES = BN * D * 2;
-  constexpr int V_BYTES = D * BN * 2;
-  constexpr int M_BYTES = MODE == kBitmask ? BM * NKB * 4 : 0;
-  constexpr int BUF = K_BYTES + V_BYTES + M_BYTES;
-  constexpr int KL = BN * KC / NT;                   // K chunks loaded per thread
-  constexpr int VPAIRS = (BN / 4) * KC;              // (key quad, d chunk) pairs per V tile
-  constexpr int VL = (VPAIRS + NT - 1) / NT;
-  constexpr int QL = BM * KC / NT;                   // Q chunks staged per thread
-  static_assert(BM * D * 2 <= 2 * BUF, "Q staging must fit in the K/V buffers");
-  static_assert(KL * NT == BN * KC && QL * NT == BM * KC, "load split");
+  constexpr int BM = kBM, BN = kBN, NT = kThreads, NW = kWaves;
+  constexpr int KC = D / 8;        // 16-byte chunks per row
+  constexpr int NKB = BN / 32;     // 32-key blocks per tile (one MFMA output block each)
+  constexpr int QKS = D / 16;      // MFMA k-steps of Q K^T
+  constexpr int NDB = D / 32;      // 32-wide blocks of head_dim in O
+  constexpr int PKS = BN / 16;     // MFMA k-steps of P V
+  using L = Lds<D>;
+  constexpr int RPR = L::RPR, RS = L::RS;
+  constexpr int NREG = BN / RPR;     // regions per tile
+  constexpr int T_BYTES = NREG * RS; // one K tile (BN rows)
+  constexpr int M_WORDS = MODE == kBitmask ? BM * NKB : 1;
+  constexpr int DMA_PER_WAVE = NREG / NW;             // one region per DMA instruction
+  constexpr int QL = BM * KC / NT;                    // Q chunks staged per thread
+  static_assert(BM == 2 * BN, "Q staging uses the two K buffers, BN rows each");
+  static_assert(DMA_PER_WAVE * NW == NREG && QL * NT == BM * KC, "load split");
 
-  __shared__ __attribute__((aligned(16))) unsigned char smem[2 * BUF];
+  // Separate arrays (not one array indexed by buffer) so the compiler can tell the DMA into one
+  // buffer from LDS reads of another and does not wait for the DMA before those reads.
+  __shared__ __attribute__((aligned(1024))) unsigned char k_lds0[T_BYTES];
+  __shared__ __attribute__((aligned(1024))) unsigned char k_lds1[T_BYTES];
+  __shared__ __attribute__((aligned(1024))) unsigned char v_lds0[T_BYTES];
+  __shared__ __attribute__((aligned(1024))) unsigned char v_lds1[T_BYTES];
+  __shared__ __attribute__((aligned(16))) u32 m_lds0[M_WORDS];
+  __shared__ __attribute__((aligned(16))) u32 m_lds1[M_WORDS];
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
-  const int l32 = lane & 31, hl = lane >> 5;  // lane column and lane half
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31, hl = lane >> 5;   // lane column and lane half
   const int S = p.S, G = p.G, Hq = p.Hq, Hkv = p.Hkv;
 
   // XCD-aware remap: the hardware deals workgroup i to XCD i % 8.  Give XCD x the contiguous
@@ -172,8 +247,7 @@ __global__ __launch_bounds__(kThreads, 2) void fa_fwd_kernel(Params p) {
   const int my_row = row0 + wave * 32 + l32;
   const int my_pos = my_row / G;
   const int my_head = hk * G + (my_row - my_pos * G);
-  const int w_row0 = row0 + wave * 32;
-  const int w_pmin = w_row0 / G;
+  const int w_pmin = (row0 + wave * 32) / G;
   const bool wave_live = w_pmin < S;
 
   int n_tiles;
@@ -184,60 +258,63 @@ __global__ __launch_bounds__(kThreads, 2) void fa_fwd_kernel(Params p) {
     n_tiles = (S + BN - 1) / BN;
   }
 
-  // ---- Q: coalesced 128-bit loads -> swizzled LDS -> MFMA B operands held in registers.
+  // Lane bases of the 128-bit operand reads (Q and K): row l32 of a 32-row block, chunk
+  // 2ks + hl.  At d=64 the row XOR depends on ks & 1, hence two bases.
+  int op_base[2];
+#pragma unroll
+  for (int e = 0; e < 2; ++e) op_base[e] = L::off(l32, 2 * e + hl);
+  // (row 32*blk + l32, chunk 2ks + hl) = op_base[ks & 1] + blk*BLK_OFF + (ks >> 1)*2*KS2_OFF
+  constexpr int BLK_OFF = (32 / RPR) * RS;
+  constexpr int KS2_OFF = 2 * RPR * 16;  // two chunks
+  auto op_addr = [&](int ks, int blk) __attribute__((always_inline)) {
+    return op_base[ks & 1] + blk * BLK_OFF + (ks >> 1) * 2 * KS2_OFF;
+  };
+
+  // ---- Q: coalesced 128-bit loads -> LDS (rows 0..63 in k_lds0, 64..127 in k_lds1) -> MFMA B
+  // operands held in registers for the whole key loop.
 #pragma unroll
   for (int i = 0; i < QL; ++i) {
     const int id = tid + NT * i, r = id / KC, c = id % KC;
     const int grow = row0 + r, pos = grow / G, h = hk * G + (grow - pos * G);
     u32x4 x = {0u, 0u, 0u, 0u};
     if (pos < S) x = *(const u32x4*)(p.q + q_batch + ((size_t)pos * Hq + h) * D + c * 8);
-    *(u32x4*)(smem + r * D * 2 + ((c ^ (r % KC)) * 16)) = x;
+    *(u32x4*)((r < BN ? k_lds0 : k_lds1) + L::off(r % BN, c)) = x;
   }
   __syncthreads();
   u32x4 qreg[QKS];
 #pragma unroll
   for (int ks = 0; ks < QKS; ++ks) {
-    const int r = wave * 32 + l32, c = 2 * ks + hl;
-    u32x4 x = *(const u32x4*)(smem + r * D * 2 + ((c ^ (r % KC)) * 16));
+    const u32x4 x = *(const u32x4*)((wave < 2 ? k_lds0 : k_lds1) + op_addr(ks, wave & 1));
     qreg[ks] = x ^ p.qflip;
   }
   __syncthreads();
 
-  // ---- K/V/mask staging: global -> registers (prefetch) -> LDS.
-  u32x4 kreg[KL];
-  u32x4 vreg[VL][4];
+  // ---- K/V staging by DMA: instruction i of this wave fills region n = i*NW + wave; lane = slot
+  // s holds chunk s / RPR of row n*RPR + ((s % RPR) ^ x(chunk)).
+  const int dma_c = lane / RPR;
+  const int dma_rr = (lane % RPR) ^ L::x(dma_c);
+  auto dma_tile = [&](const uint16_t* __restrict__ src, int j, unsigned char* dst)
+                      __attribute__((always_inline)) {
+    const int k0 = j * BN;
+#pragma unroll
+    for (int i = 0; i < DMA_PER_WAVE; ++i) {
+      const int n = i * NW + wave;
+      const int key = min(k0 + n * RPR + dma_rr, S - 1);
+      __builtin_amdgcn_global_load_lds((const void*)(src + key * kv_stride + dma_c * 8),
+                                       (lds_void*)(dst + n * RS), 16, 0, 0);
+    }
+  };
+
+  // Mask words (bitmask mode): thread t < BM stages the NKB words of row t for a tile.
   u32 mreg[NKB];
-  const u32* mrow = nullptr;  // mask row of the row this thread stages (bitmask mode)
+  const u32* mrow = nullptr;
   bool mrow_ok = false;
   if (MODE == kBitmask && tid < BM) {
     const int grow = row0 + tid, pos = grow / G, h = hk * G + (grow - pos * G);
     mrow_ok = pos < S;
     if (mrow_ok) mrow = p.mask + (((size_t)b * Hq + h) * S + pos) * (size_t)p.W;
   }
-
-  auto gload = [&](int j) {
-    const int k0 = j * BN;
-#pragma unroll
-    for (int i = 0; i < KL; ++i) {
-      const int id = tid + NT * i, r = id / KC, c = id % KC, key = k0 + r;
-      u32x4 x = {0u, 0u, 0u, 0u};
-      if (key < S) x = *(const u32x4*)(kg + key * kv_stride + c * 8);
-      kreg[i] = x;
-    }
-#pragma unroll
-    for (int i = 0; i < VL; ++i) {
-      const int id = tid + NT * i;
-      if (VPAIRS % NT == 0 || id < VPAIRS) {
-        const int quad = id / KC, c = id % KC;
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-          const int key = k0 + 4 * quad + kk;
-          u32x4 x = {0u, 0u, 0u, 0u};
-          if (key < S) x = *(const u32x4*)(vg + key * kv_stride + c * 8);
-          vreg[i][kk] = x;
-        }
-      }
-    }
+  auto mask_load = [&](int j) __attribute__((always_inline)) {
     if (MODE == kBitmask && tid < BM) {
 #pragma unroll
       for (int w = 0; w < NKB; ++w) {
@@ -246,44 +323,44 @@ __global__ __launch_bounds__(kThreads, 2) void fa_fwd_kernel(Params p) {
       }
     }
   };
-
-  auto lstore = [&](int buf) {
-    unsigned char* kb = smem + buf * BUF;
-    unsigned char* vb = kb + K_BYTES;
-#pragma unroll
-    for (int i = 0; i < KL; ++i) {
-      const int id = tid + NT * i, r = id / KC, c = id % KC;
-      *(u32x4*)(kb + r * D * 2 + ((c ^ (r % KC)) * 16)) = kreg[i];
-    }
-#pragma unroll
-    for (int i = 0; i < VL; ++i) {
-      const int id = tid + NT * i;
-      if (VPAIRS % NT == 0 || id < VPAIRS) {
-        const int quad = id / KC, c = id % KC;
-        // Key quad -> position in the transposed row.  Within every 16 keys the quads are
-        // stored in the order 0, 2, 1, 3 so that the 8 keys one MFMA lane half needs for P V
-        // (keys 4h..4h+3 and 8+4h..8+4h+3) are 16 contiguous bytes.
-        const int qq = quad & 3;
-        const int pos0 = 16 * (quad >> 2) + ((qq & 1) << 3) + ((qq & 2) << 1);
-        const int cc = pos0 >> 3, off = (pos0 & 7) * 2;
-#pragma unroll
-        for (int m = 0; m < 4; ++m) {
-          const u32 x0 = vreg[i][0][m], x1 = vreg[i][1][m], x2 = vreg[i][2][m], x3 = vreg[i][3][m];
-          const u32x2 lo = {__builtin_amdgcn_perm(x1, x0, 0x05040100u),
-                            __builtin_amdgcn_perm(x3, x2, 0x05040100u)};
-          const u32x2 hi = {__builtin_amdgcn_perm(x1, x0, 0x07060302u),
-                            __builtin_amdgcn_perm(x3, x2, 0x07060302u)};
-          const int d0 = 8 * c + 2 * m, d1 = d0 + 1;
-          *(u32x2*)(vb + d0 * BN * 2 + ((cc ^ (d0 % VC)) * 16) + off) = lo;
-          *(u32x2*)(vb + d1 * BN * 2 + ((cc ^ (d1 % VC)) * 16) + off) = hi;
-        }
-      }
-    }
+  auto mask_store = [&](u32* mb) __attribute__((always_inline)) {
     if (MODE == kBitmask && tid < BM) {
-      u32* mb = (u32*)(vb + V_BYTES);
 #pragma unroll
       for (int w = 0; w < NKB; ++w) mb[tid * NKB + w] = mreg[w];
     }
+  };
+
+  // Tile class of tile j for this wave: full (no masking), skip (a 64-lane ballot finds no kept
+  // bit), or partial with per-lane keep words.  Lane half hl holds keys 8*(r/4) + 4*hl + r%4 of
+  // each 32-key block, so the word is pre-shifted by 4*hl and register r tests the constant bit
+  // 8*(r/4) + r%4.
+  struct Cls {
+    u32 wsh[NKB];
+    bool full, skip;
+  };
+  auto classify = [&](int j, const u32* mb) __attribute__((always_inline)) {
+    Cls cl;
+    const int k0 = j * BN;
+    if (MODE == kNone) cl.full = k0 + BN <= S;
+    else if (MODE == kCausal) cl.full = k0 + BN - 1 <= w_pmin;
+    else cl.full = false;
+    cl.skip = false;
+#pragma unroll
+    for (int kb32 = 0; kb32 < NKB; ++kb32) cl.wsh[kb32] = ~0u;
+    if (!cl.full) {
+      u32 any = 0;
+#pragma unroll
+      for (int kb32 = 0; kb32 < NKB; ++kb32) {
+        const int kbase = k0 + 32 * kb32;
+        u32 w = low_bits(S - kbase);
+        if (MODE == kCausal) w = my_pos < S ? (w & low_bits(my_pos - kbase + 1)) : 0u;
+        if (MODE == kBitmask) w &= mb[(wave * 32 + l32) * NKB + kb32];
+        any |= w;
+        cl.wsh[kb32] = w >> (4 * hl);
+      }
+      cl.skip = __ballot(any != 0u) == 0ull;
+    }
+    return cl;
   };
 
   f32x16 oacc[NDB];
@@ -295,129 +372,145 @@ __global__ __launch_bounds__(kThreads, 2) void fa_fwd_kernel(Params p) {
   float l_run = 0.f;     // this lane's partial row sum (its 16 keys of each 32-key block)
   const float c = p.c;
 
-  gload(0);
-  lstore(0);
-  __syncthreads();
+  // V^T operand (A of O^T += V^T P^T) from two ds_read_b64_tr_b16.  That instruction transposes
+  // 16-bit elements across each 16-lane group: lane j of the group receives element j%4 of the
+  // 8 bytes addressed by lanes j/4 + 4t, t = 0..3.  Lane l (group q = l/16, index i = l%16)
+  // therefore points at key row 4*hl + i/4 (+16 per k-step, +8 for the second read) and
+  // head_dim column 16*(q&1) + 4*(i&3) (+32 per head_dim block), and receives the 4 keys of its
+  // column 32*db + l%32 in the key order of the P register slots.
+  const int tr_row = 4 * hl + ((lane & 15) >> 2);
+  const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  const int tr_base = L::off(tr_row, tr_col >> 3) + (tr_col & 7) * 2;
+  constexpr int TR_KS = (16 / RPR) * RS, TR_H = (8 / RPR) * RS, TR_DB = 4 * RPR * 16;
+  auto v_operand = [&](const unsigned char* vb, int ks, int db) __attribute__((always_inline)) {
+    const int oa = tr_base + ks * TR_KS + db * TR_DB;
+    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vb + oa));
+    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vb + oa + TR_H));
+    const u32x2 lo2 = __builtin_bit_cast(u32x2, lo), hi2 = __builtin_bit_cast(u32x2, hi);
+    return (u32x4){lo2[0], lo2[1], hi2[0], hi2[1]};
+  };
 
-  for (int j = 0; j < n_tiles; ++j) {
-    const int buf = j & 1;
-    if (j + 1 < n_tiles) gload(j + 1);
-
-    if (wave_live) {
-      const unsigned char* kb = smem + buf * BUF;
-      const unsigned char* vb = kb + K_BYTES;
-      const int k0 = j * BN;
-
-      // Tile class for this wave: full (no masking), partial (per-element keep bits) or
-      // empty (ballot finds no kept bit: skipped).
-      bool full;
-      if (MODE == kNone) full = k0 + BN <= S;
-      else if (MODE == kCausal) full = k0 + BN - 1 <= w_pmin;
-      else full = false;
-
-      u32 wsh[NKB];
-      bool skip = false;
-      if (!full) {
-        u32 any = 0;
+  // One tile's compute: S^T = K Q^T (operands read one k-step ahead), masked online softmax,
+  // O = alpha O + V^T P^T (branch-free rescale, P straight from registers; P slots 0..3 of lane
+  // half hl hold keys 16ks + 4hl + 0..3 and slots 4..7 keys 16ks + 8 + 4hl + 0..3, the keys the
+  // two transposing reads deliver).
+  auto compute = [&](const Cls& cls, const unsigned char* kb, const unsigned char* vb)
+                     __attribute__((always_inline)) {
+    f32x16 sacc[NKB];
 #pragma unroll
-        for (int kb32 = 0; kb32 < NKB; ++kb32) {
-          const int kbase = k0 + 32 * kb32;
-          u32 w = low_bits(S - kbase);
-          if (MODE == kCausal) w = my_pos < S ? (w & low_bits(my_pos - kbase + 1)) : 0u;
-          if (MODE == kBitmask) w &= ((const u32*)(vb + V_BYTES))[(wave * 32 + l32) * NKB + kb32];
-          any |= w;
-          // Lane half hl holds keys 8*(r/4) + 4*hl + r%4 of the block: pre-shift by 4*hl so
-          // register r tests the constant bit 8*(r/4) + r%4.
-          wsh[kb32] = w >> (4 * hl);
-        }
-        skip = __ballot(any != 0u) == 0ull;
+    for (int kb32 = 0; kb32 < NKB; ++kb32)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sacc[kb32][r] = 0.f;
+    u32x4 ka[2][NKB];
+#pragma unroll
+    for (int kb32 = 0; kb32 < NKB; ++kb32) ka[0][kb32] = *(const u32x4*)(kb + op_addr(0, kb32));
+#pragma unroll
+    for (int ks = 0; ks < QKS; ++ks) {
+      if (ks + 1 < QKS) {
+#pragma unroll
+        for (int kb32 = 0; kb32 < NKB; ++kb32)
+          ka[(ks + 1) & 1][kb32] = *(const u32x4*)(kb + op_addr(ks + 1, kb32));
       }
-
-      if (!skip) {
-        // S^T = K Q^T on the matrix cores.
-        f32x16 sacc[NKB];
 #pragma unroll
-        for (int kb32 = 0; kb32 < NKB; ++kb32)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) sacc[kb32][r] = 0.f;
-#pragma unroll
-        for (int ks = 0; ks < QKS; ++ks) {
-#pragma unroll
-          for (int kb32 = 0; kb32 < NKB; ++kb32) {
-            const int r = 32 * kb32 + l32, cch = 2 * ks + hl;
-            const u32x4 a = *(const u32x4*)(kb + r * D * 2 + ((cch ^ (r % KC)) * 16));
-            sacc[kb32] = mfma32<BF16>(a, qreg[ks], sacc[kb32]);
-          }
-        }
-
-        // Masked scores -> -inf (bit-field extract of the keep bit, bit-field insert).
-        if (!full) {
-#pragma unroll
-          for (int kb32 = 0; kb32 < NKB; ++kb32)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const int bit = 8 * (r >> 2) + (r & 3);
-              const int keep = ((int)(wsh[kb32] << (31 - bit))) >> 31;
-              sacc[kb32][r] = __int_as_float((__float_as_int(sacc[kb32][r]) & keep) |
-                                             (~keep & (int)0xff800000));
-            }
-        }
-
-        // Row max: in-lane, then across the two lane halves.
-        float mx = -INFINITY;
-#pragma unroll
-        for (int kb32 = 0; kb32 < NKB; ++kb32)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb32][r]);
-        mx = max_halves(mx);
-        const float m_new = fmaxf(m_run, mx * c);
-        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-        m_run = m_new;
-
-        // p = 2^(s*c - m); partial row sum; P rounded to the input dtype for P V.
-        float psum = 0.f;
-#pragma unroll
-        for (int kb32 = 0; kb32 < NKB; ++kb32)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const float e = __builtin_amdgcn_exp2f(fmaf(sacc[kb32][r], c, -m_new));
-            sacc[kb32][r] = e;
-            psum += e;
-          }
-        l_run = l_run * alpha + psum;
-
-        // Branch-free rescale of the O accumulator.
-#pragma unroll
-        for (int db = 0; db < NDB; ++db)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
-
-        u32x4 pk[PKS];
-#pragma unroll
-        for (int kb32 = 0; kb32 < NKB; ++kb32)
-#pragma unroll
-          for (int h = 0; h < 2; ++h) {
-            f32x8 t;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) t[e] = sacc[kb32][8 * h + e];
-            pk[2 * kb32 + h] = pack8<BF16>(t);
-          }
-
-        // O^T += V^T P^T on the matrix cores; P comes straight from registers.
-#pragma unroll
-        for (int ks = 0; ks < PKS; ++ks) {
-#pragma unroll
-          for (int db = 0; db < NDB; ++db) {
-            const int r = 32 * db + l32, cch = 2 * ks + hl;
-            const u32x4 a = *(const u32x4*)(vb + r * BN * 2 + ((cch ^ (r % VC)) * 16));
-            oacc[db] = mfma32<BF16>(a, pk[ks], oacc[db]);
-          }
-        }
-      }
+      for (int kb32 = 0; kb32 < NKB; ++kb32)
+        sacc[kb32] = mfma32<BF16>(ka[ks & 1][kb32], qreg[ks], sacc[kb32]);
     }
 
-    if (j + 1 < n_tiles) lstore(buf ^ 1);
+    if (!cls.full) {  // masked scores -> -inf: bit-field extract of the keep bit + bit-field insert
+#pragma unroll
+      for (int kb32 = 0; kb32 < NKB; ++kb32)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int bit = 8 * (r >> 2) + (r & 3);
+          const int keep = ((int)(cls.wsh[kb32] << (31 - bit))) >> 31;
+          sacc[kb32][r] = __int_as_float((__float_as_int(sacc[kb32][r]) & keep) |
+                                         (~keep & (int)0xff800000));
+        }
+    }
+    // Row max: four independent in-lane chains of 3-input maxima (v_max3_f32) over 8 scores
+    // each, then across the two lane halves.
+    float mx4[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const f32x16& v = sacc[(q >> 1) % NKB];
+      const int b0 = 8 * (q & 1);
+      float m = __builtin_fmaxf(__builtin_fmaxf(v[b0], v[b0 + 1]), v[b0 + 2]);
+      m = __builtin_fmaxf(__builtin_fmaxf(m, v[b0 + 3]), v[b0 + 4]);
+      m = __builtin_fmaxf(__builtin_fmaxf(m, v[b0 + 5]), v[b0 + 6]);
+      mx4[q] = __builtin_fmaxf(m, v[b0 + 7]);
+    }
+    float mx = __builtin_fmaxf(__builtin_fmaxf(mx4[0], mx4[1]), __builtin_fmaxf(mx4[2], mx4[3]));
+    mx = max_halves(mx);
+    const float m_new = fmaxf(m_run, mx * c);
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+    m_run = m_new;
+    // p = 2^(s*c - m), rounded to the input dtype; the row sum adds the rounded values
+    // (v_dot2 against (1, 1)) so numerator and denominator see the same P.
+    u32x4 pk[PKS];
+    float ps[2] = {0.f, 0.f};
+#pragma unroll
+    for (int kb32 = 0; kb32 < NKB; ++kb32)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        f32x8 t;
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          t[e] = __builtin_amdgcn_exp2f(fmaf(sacc[kb32][8 * h + e], c, -m_new));
+        const u32x4 pw = pack8<BF16>(t);
+        pk[2 * kb32 + h] = pw;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) ps[e & 1] = dot2_ones<BF16>(pw[e], ps[e & 1]);
+      }
+    l_run = l_run * alpha + (ps[0] + ps[1]);
+
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+    u32x4 va[2][NDB];
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) va[0][db] = v_operand(vb, 0, db);
+#pragma unroll
+    for (int ks = 0; ks < PKS; ++ks) {
+      if (ks + 1 < PKS) {
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+          va[(ks + 1) & 1][db] = v_operand(vb, ks + 1, db);
+      }
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) oacc[db] = mfma32<BF16>(va[ks & 1][db], pk[ks], oacc[db]);
+    }
+  };
+
+  // One tile: prefetch tile j+1 (K and V by DMA, mask words into registers), compute tile j,
+  // then wait for this wave's loads, store the mask words and meet the other waves at the
+  // barrier.
+  auto tile = [&](int j, const unsigned char* k_cur, const unsigned char* v_cur,
+                  const u32* m_cur, unsigned char* k_fill, unsigned char* v_fill, u32* m_fill)
+                  __attribute__((always_inline)) {
+    const bool more = j + 1 < n_tiles;
+    if (more) {
+      dma_tile(kg, j + 1, k_fill);
+      dma_tile(vg, j + 1, v_fill);
+      mask_load(j + 1);
+    }
+    const Cls cls = classify(j, m_cur);
+    if (wave_live && !cls.skip) compute(cls, k_cur, v_cur);
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's DMA and loads have landed
+    if (more) mask_store(m_fill);
     __syncthreads();
+  };
+
+  // Prologue: tile 0.
+  dma_tile(kg, 0, k_lds0);
+  dma_tile(vg, 0, v_lds0);
+  mask_load(0);
+  mask_store(m_lds0);
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+  __syncthreads();
+  for (int j = 0; j < n_tiles; j += 2) {
+    tile(j, k_lds0, v_lds0, m_lds0, k_lds1, v_lds1, m_lds1);
+    if (j + 1 < n_tiles) tile(j + 1, k_lds1, v_lds1, m_lds1, k_lds0, v_lds0, m_lds0);
   }
 
   // ---- Epilogue: O / l (0 for a row with no kept key), rounded, 8-byte stores.

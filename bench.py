@@ -96,6 +96,9 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=12.0,
                     help="seconds of oracle work for the CPU baseline (0 = skip)")
     ap.add_argument("--no-also", action="store_true", help="skip the causal companion timing")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="first run a plain 512 MiB device copy three times, so hardware byte "
+                         "counters can be scaled by a kernel of known traffic")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -111,6 +114,14 @@ def main():
     q, k, v = inputs.make_qkv(w)
     qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
     out = torch.empty_like(qd)
+
+    if args.copy_calibration:
+        src = torch.empty(512 << 20, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     def step(mode=w.mode):
         fa_fwd(qd, kd, vd, mode=mode, scale=w.scale, out=out)
