@@ -178,13 +178,15 @@ struct Lds {
 // tile, 128 bytes, as 8 "units" of 16 bytes.  Unit u = 2ks + hl holds keys 16ks + 4hl + 0..3
 // (first 8 bytes) and 16ks + 8 + 4hl + 0..3 (last 8 bytes): exactly the 8 keys, in register
 // order, that lane half hl of an MFMA needs at k-step ks of P V, so each V^T operand is one
-// 128-bit read.  Row d lives in 256-byte line d/2, half h(d) = (d ^ d/4) & 1, with unit u at
-// slot u ^ f(d), f(d) = (d/2) & 7.  With 64 banks x 4 B, the operand reads (16 lanes, one unit
-// of 16 consecutive rows) and the staging writes (32 lanes, two whole rows d and d+4) touch
-// every bank once.  The read address is a per-lane base XOR 32*ks, plus 4096 per 32-row block.
+// 128-bit read.  Rows d and d ^ 8 share the 256-byte line ((d/16) * 8 + d % 8); unit u of row d
+// sits at 16-byte slot u ^ g(d), g(d) = (d % 16) ^ ((d / 16) % 8) (bit 3 of the slot is bit 3
+// of d).  With 64 banks x 4 B, the operand reads (16 lanes: one unit of 16 consecutive rows)
+// and the staging writes (32 lanes: one half-unit of 16 rows spaced 8 apart, both halves) touch
+// every bank once.  The read address of k-step ks is a per-(lane, 32-row block) base XOR 32*ks.
 struct VtLds {
   __device__ static constexpr int off(int d, int u, int half) {
-    return (d >> 1) * 256 + ((d ^ (d >> 2)) & 1) * 128 + ((u ^ ((d >> 1) & 7)) * 16) + half * 8;
+    return ((((d >> 4) << 3) | (d & 7)) * 256) + ((u ^ ((d & 15) ^ ((d >> 4) & 7))) & 15) * 16 +
+           half * 8;
   }
 };
 
@@ -204,18 +206,22 @@ __global__ __launch_bounds__(kThreads, 2) void fa_fwd_kernel(Params p) {
   constexpr int RPR = L::RPR, RS = L::RS;
   constexpr int NREG = BN / RPR;     // regions per tile
   constexpr int T_BYTES = NREG * RS; // one K tile (BN rows)
+  constexpr int VT_BYTES = D * 128;  // one transposed V tile (D rows of BN = 64 keys)
+  constexpr int NDQ = D / 8;         // 16-byte column chunks of a V row
+  constexpr int VS_THREADS = 16 * NDQ;  // V staging: one key quad x one column chunk each
   constexpr int M_WORDS = MODE == kBitmask ? BM * NKB : 1;
   constexpr int DMA_PER_WAVE = NREG / NW;             // one region per DMA instruction
   constexpr int QL = BM * KC / NT;                    // Q chunks staged per thread
   static_assert(BM == 2 * BN, "Q staging uses the two K buffers, BN rows each");
   static_assert(DMA_PER_WAVE * NW == NREG && QL * NT == BM * KC, "load split");
+  static_assert(BN == 64 && VS_THREADS <= NT, "V staging covers a 64-key tile");
 
   // Separate arrays (not one array indexed by buffer) so the compiler can tell the DMA into one
   // buffer from LDS reads of another and does not wait for the DMA before those reads.
   __shared__ __attribute__((aligned(1024))) unsigned char k_lds0[T_BYTES];
   __shared__ __attribute__((aligned(1024))) unsigned char k_lds1[T_BYTES];
-  __shared__ __attribute__((aligned(1024))) unsigned char v_lds0[T_BYTES];
-  __shared__ __attribute__((aligned(1024))) unsigned char v_lds1[T_BYTES];
+  __shared__ __attribute__((aligned(1024))) unsigned char v_lds0[VT_BYTES];  // V^T tiles
+  __shared__ __attribute__((aligned(1024))) unsigned char v_lds1[VT_BYTES];
   __shared__ __attribute__((aligned(16))) u32 m_lds0[M_WORDS];
   __shared__ __attribute__((aligned(16))) u32 m_lds1[M_WORDS];
 
@@ -305,6 +311,41 @@ __global__ __launch_bounds__(kThreads, 2) void fa_fwd_kernel(Params p) {
     }
   };
 
+  // ---- V staging (transposed).  Thread t < VS_THREADS owns column chunk dq (head_dim
+  // 8dq..8dq+7) of key quad q (keys 4q..4q+3).  Consecutive lanes take consecutive column
+  // chunks of one key row, so every load instruction reads whole rows.  Lanes 16-31 take quad
+  // q+2 (same V^T unit, other half) so the two 16-lane halves of a write never share a bank.
+  // The four 16-byte pieces (one per key) are loaded into registers early, then transposed with
+  // byte permutes into eight 8-byte pieces (one per column) and written at their V^T unit:
+  // unit 2(q/4) + (q%2), half (q/2)%2.
+  const int vs_dq = D == 128 ? (tid & 15) : (tid & 7);
+  const int vs_qi = D == 128 ? (tid >> 4) : (tid >> 3);
+  const int vs_q = 4 * (vs_qi >> 2) + ((vs_qi >> 1) & 1) + 2 * (vs_qi & 1);
+  u32x4 vstage[4];
+  auto v_load = [&](int j) __attribute__((always_inline)) {
+    if (tid < VS_THREADS) {
+      const int k0 = j * BN;
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        const int key = min(k0 + 4 * vs_q + kk, S - 1);
+        vstage[kk] = *(const u32x4*)(vg + key * kv_stride + 8 * vs_dq);
+      }
+    }
+  };
+  auto v_store = [&](unsigned char* vt) __attribute__((always_inline)) {
+    if (tid < VS_THREADS) {
+      const int u = 2 * (vs_q >> 2) + (vs_q & 1), half = (vs_q >> 1) & 1;
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj) {
+        const int m = jj >> 1;
+        const u32 sel = (jj & 1) ? 0x07060302u : 0x05040100u;  // high / low 16-bit halves
+        const u32x2 col = {__builtin_amdgcn_perm(vstage[1][m], vstage[0][m], sel),
+                           __builtin_amdgcn_perm(vstage[3][m], vstage[2][m], sel)};
+        *(u32x2*)(vt + VtLds::off(8 * vs_dq + jj, u, half)) = col;
+      }
+    }
+  };
+
   // Mask words (bitmask mode): thread t < BM stages the NKB words of row t for a tile.
   u32 mreg[NKB];
   const u32* mrow = nullptr;
@@ -372,28 +413,19 @@ __global__ __launch_bounds__(kThreads, 2) void fa_fwd_kernel(Params p) {
   float l_run = 0.f;     // this lane's partial row sum (its 16 keys of each 32-key block)
   const float c = p.c;
 
-  // V^T operand (A of O^T += V^T P^T) from two ds_read_b64_tr_b16.  That instruction transposes
-  // 16-bit elements across each 16-lane group: lane j of the group receives element j%4 of the
-  // 8 bytes addressed by lanes j/4 + 4t, t = 0..3.  Lane l (group q = l/16, index i = l%16)
-  // therefore points at key row 4*hl + i/4 (+16 per k-step, +8 for the second read) and
-  // head_dim column 16*(q&1) + 4*(i&3) (+32 per head_dim block), and receives the 4 keys of its
-  // column 32*db + l%32 in the key order of the P register slots.
-  const int tr_row = 4 * hl + ((lane & 15) >> 2);
-  const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-  const int tr_base = L::off(tr_row, tr_col >> 3) + (tr_col & 7) * 2;
-  constexpr int TR_KS = (16 / RPR) * RS, TR_H = (8 / RPR) * RS, TR_DB = 4 * RPR * 16;
+  // V^T operand (A of O^T += V^T P^T): lane l reads head_dim row 32*db + l%32, unit 2ks + hl,
+  // at a per-block base XOR 32*ks.
+  int vt_base[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) vt_base[db] = VtLds::off(32 * db + l32, hl, 0);
   auto v_operand = [&](const unsigned char* vb, int ks, int db) __attribute__((always_inline)) {
-    const int oa = tr_base + ks * TR_KS + db * TR_DB;
-    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vb + oa));
-    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vb + oa + TR_H));
-    const u32x2 lo2 = __builtin_bit_cast(u32x2, lo), hi2 = __builtin_bit_cast(u32x2, hi);
-    return (u32x4){lo2[0], lo2[1], hi2[0], hi2[1]};
+    return *(const u32x4*)(vb + (vt_base[db] ^ (32 * ks)));
   };
 
   // One tile's compute: S^T = K Q^T (operands read one k-step ahead), masked online softmax,
   // O = alpha O + V^T P^T (branch-free rescale, P straight from registers; P slots 0..3 of lane
-  // half hl hold keys 16ks + 4hl + 0..3 and slots 4..7 keys 16ks + 8 + 4hl + 0..3, the keys the
-  // two transposing reads deliver).
+  // half hl hold keys 16ks + 4hl + 0..3 and slots 4..7 keys 16ks + 8 + 4hl + 0..3, the key order
+  // of a V^T unit).
   auto compute = [&](const Cls& cls, const unsigned char* kb, const unsigned char* vb)
                      __attribute__((always_inline)) {
     f32x16 sacc[NKB];
@@ -482,31 +514,35 @@ __global__ __launch_bounds__(kThreads, 2) void fa_fwd_kernel(Params p) {
     }
   };
 
-  // One tile: prefetch tile j+1 (K and V by DMA, mask words into registers), compute tile j,
-  // then wait for this wave's loads, store the mask words and meet the other waves at the
-  // barrier.
+  // One tile: prefetch tile j+1 (K by DMA, V and mask words into registers), compute tile j,
+  // then wait for this wave's loads, write V^T and the mask words and meet the other waves at
+  // the barrier.
   auto tile = [&](int j, const unsigned char* k_cur, const unsigned char* v_cur,
                   const u32* m_cur, unsigned char* k_fill, unsigned char* v_fill, u32* m_fill)
                   __attribute__((always_inline)) {
     const bool more = j + 1 < n_tiles;
     if (more) {
       dma_tile(kg, j + 1, k_fill);
-      dma_tile(vg, j + 1, v_fill);
+      v_load(j + 1);
       mask_load(j + 1);
     }
     const Cls cls = classify(j, m_cur);
     if (wave_live && !cls.skip) compute(cls, k_cur, v_cur);
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's DMA and loads have landed
-    if (more) mask_store(m_fill);
+    if (more) {
+      v_store(v_fill);
+      mask_store(m_fill);
+    }
     __syncthreads();
   };
 
   // Prologue: tile 0.
   dma_tile(kg, 0, k_lds0);
-  dma_tile(vg, 0, v_lds0);
+  v_load(0);
   mask_load(0);
   mask_store(m_lds0);
   __builtin_amdgcn_s_waitcnt(0x0F70);
+  v_store(v_lds0);
   __syncthreads();
   for (int j = 0; j < n_tiles; j += 2) {
     tile(j, k_lds0, v_lds0, m_lds0, k_lds1, v_lds1, m_lds1);

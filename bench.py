@@ -97,8 +97,8 @@ def main():
                     help="seconds of oracle work for the CPU baseline (0 = skip)")
     ap.add_argument("--no-also", action="store_true", help="skip the causal companion timing")
     ap.add_argument("--copy-calibration", action="store_true",
-                    help="first run a plain 512 MiB device copy three times, so hardware byte "
-                         "counters can be scaled by a kernel of known traffic")
+                    help="first run a plain elementwise kernel (512 MiB read, 512 MiB written) three "
+                         "times, so hardware byte counters can be scaled by a kernel of known traffic")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -116,10 +116,11 @@ def main():
     out = torch.empty_like(qd)
 
     if args.copy_calibration:
+        # A plain elementwise kernel of known traffic: reads 512 MiB, writes 512 MiB.
         src = torch.empty(512 << 20, dtype=torch.uint8, device=dev).fill_(1)
         dst = torch.empty_like(src)
         for _ in range(3):
-            dst.copy_(src)
+            torch.add(src, 1, out=dst)
         torch.cuda.synchronize()
         del src, dst
 
