@@ -141,15 +141,17 @@ def main():
             "frac_of_peak": fc / (ms_c * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
 
     bytes_alg = 4 * w.batch * w.seq_len * w.n_q_heads * w.head_dim * 2   # Q, K, V read + O written
+    # HBM bytes per launch measured with rocprofv3 byte counters (profiles/traffic.json); only
+    # reported while the kernel source is the one the counters were taken on.
     traffic = None
     tfile = os.path.join(ROOT, "profiles", "traffic.json")
     if os.path.exists(tfile):
-        try:
-            tr = json.load(open(tfile))
-            key = f"{w.mode}:B{w.batch}:S{w.seq_len}:H{w.n_q_heads}:d{w.head_dim}"
-            traffic = tr.get(key)
-        except Exception:
-            traffic = None
+        import hashlib
+        src = os.path.join(ROOT, "attention_forward_fwd_amd", "csrc", "fa_fwd.hip")
+        sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+        tr = json.load(open(tfile))
+        if tr.get("kernel_source_sha256") == sha:
+            traffic = tr.get(f"{w.mode}:B{w.batch}:S{w.seq_len}:H{w.n_q_heads}:d{w.head_dim}")
     rec = {
         "metric": METRIC,
         "value": tflops,
