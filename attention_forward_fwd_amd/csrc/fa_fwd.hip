@@ -28,15 +28,15 @@
 //     touches only the lane's own query.  P never leaves registers: the S^T accumulator layout
 //     is re-used directly as the B operand of the P V product (keys permuted consistently on
 //     both operands).
-//   * LDS: K and V tiles are copied global -> LDS by the DMA path (global_load_lds_dwordx4, no
-//     registers), row-major [BN][D] with 16-byte chunks XOR-swizzled by row; the swizzle is
-//     applied to the global addresses since the DMA writes LDS in lane order.  K operands are
-//     128-bit ds_reads; V operands come from ds_read_b64_tr_b16, which transposes 16-bit
-//     elements across each 16-lane group (lane j of the group receives element j%4 of lanes
-//     j/4 + 4t, t = 0..3), turning 4 key rows of V into the 4 keys one MFMA lane needs at its
-//     head_dim column.  K/V/mask tiles are double-buffered, one workgroup barrier per tile.
-//     Key rows past the sequence end are loaded from the last valid row (address clamp) and
-//     masked, so their probabilities are exactly 0.
+//   * LDS: K tiles are copied global -> LDS by the DMA path (global_load_lds_dwordx4, no
+//     registers) into 1 KiB regions of whole rows, padded so the 128-bit operand reads are
+//     conflict-free (layout below).  V tiles are read with coalesced 128-bit loads into
+//     registers one tile ahead, transposed in registers with byte permutes and written as V^T
+//     in a layout where every P V operand (8 keys of one head_dim column, in the key order of
+//     the P registers) is a single 128-bit read.  Q is staged once through the same LDS.  K, V
+//     and mask tiles are double-buffered, one workgroup barrier per tile.  Key rows past the
+//     sequence end are loaded from the last valid row (address clamp) and masked, so their
+//     probabilities are exactly 0.
 //   * Softmax: exp2 with log2(e) folded into the scale, running max floored at -1e30 so a
 //     fully masked row never makes NaN, unconditional (branch-free) rescale of O and l every
 //     tile, masked scores set to -inf with one bit-field extract and one bit-field insert.
@@ -88,10 +88,6 @@ constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * 64;
 constexpr int kBM = kWaves * 32;  // rows per workgroup
 constexpr int kBN = 64;           // keys per tile
-#ifndef FA_PREFETCH
-#define FA_PREFETCH 1
-#endif
-constexpr int kPrefetch = FA_PREFETCH;  // matrix-phase operand steps read ahead
 
 template <bool BF16>
 __device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
@@ -149,18 +145,19 @@ __device__ __forceinline__ u32 low_bits(int n) {
   return n >= 32 ? ~0u : (n <= 0 ? 0u : ((1u << n) - 1u));
 }
 
-// LDS layout of a K, V or Q tile (rows = keys or query rows, 16-byte chunks of head_dim).
+// LDS layout of a K or Q tile (rows = keys or query rows, 16-byte chunks of head_dim).
 // A "region" is the 1 KiB one wave-wide DMA instruction writes (lane i -> byte 16 i): it holds
 // RPR whole rows (4 at d=128, 8 at d=64), chunk c of row rr at slot c*RPR + (rr ^ x(c)), and
 // regions are padded to a stride of RS bytes.  Why:
 //   * a DMA instruction reads RPR complete rows, 1 KiB contiguous per row group (coalesced);
 //   * every operand address is a per-lane base plus compile-time offsets for the k-step, the
-//     32-key block, the head_dim block and the buffer, so no per-read address registers;
-//   * with 64 banks x 4 B: the 128-bit operand reads (16 lanes, one chunk of 16 consecutive
-//     rows) and the transposing reads (32 lanes, 4 consecutive chunks of 4 consecutive rows)
-//     touch every bank at most once per 256 bytes.  The padding shifts consecutive regions by
-//     16 (d=128) or 32 (d=64) banks; at d=64 the row index is also XORed with bit 1 of the
-//     chunk (x(c) = 4 * ((c >> 1) & 1)), since a d=64 region spans two bank lines.
+//     32-key block and the buffer, so no per-read address registers;
+//   * with 64 banks x 4 B, a 128-bit operand read (16 lanes per LDS cycle: one chunk of 16
+//     consecutive rows) touches every bank once: the RPR rows of a region sit in consecutive
+//     slots and the padding shifts consecutive regions by 16 (d=128) or 32 (d=64) banks.  At
+//     d=64 the row index within the region is also XORed with bit 1 of the chunk (x(c) =
+//     4 * ((c >> 1) & 1)); that only permutes the slots of one row group and is neutral for
+//     these reads.
 template <int D>
 struct Lds {
   static constexpr int RB = D * 2;              // bytes of one row's data
@@ -190,8 +187,6 @@ struct VtLds {
   }
 };
 
-typedef short i16x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 typedef __attribute__((address_space(3))) void lds_void;
 
 template <bool BF16, int D, int MODE>
