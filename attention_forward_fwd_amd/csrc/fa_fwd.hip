@@ -51,6 +51,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "fa.h"
 
 namespace {
@@ -88,6 +90,9 @@ constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * 64;
 constexpr int kBM = kWaves * 32;  // rows per workgroup
 constexpr int kBN = 64;           // keys per tile
+#ifndef FA_P1_VALU
+#define FA_P1_VALU 8
+#endif
 
 template <bool BF16>
 __device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
@@ -171,23 +176,42 @@ struct Lds {
   }
 };
 
-// LDS layout of a transposed V tile: row d (one head_dim index) holds the BN = 64 keys of the
-// tile, 128 bytes, as 8 "units" of 16 bytes.  Unit u = 2ks + hl holds keys 16ks + 4hl + 0..3
-// (first 8 bytes) and 16ks + 8 + 4hl + 0..3 (last 8 bytes): exactly the 8 keys, in register
-// order, that lane half hl of an MFMA needs at k-step ks of P V, so each V^T operand is one
-// 128-bit read.  Rows d and d ^ 8 share the 256-byte line ((d/16) * 8 + d % 8); unit u of row d
-// sits at 16-byte slot u ^ g(d), g(d) = (d % 16) ^ ((d / 16) % 8) (bit 3 of the slot is bit 3
-// of d).  With 64 banks x 4 B, the operand reads (16 lanes: one unit of 16 consecutive rows)
-// and the staging writes (32 lanes: one half-unit of 16 rows spaced 8 apart, both halves) touch
-// every bank once.  The read address of k-step ks is a per-(lane, 32-row block) base XOR 32*ks.
-struct VtLds {
-  __device__ static constexpr int off(int d, int u, int half) {
-    return ((((d >> 4) << 3) | (d & 7)) * 256) + ((u ^ ((d & 15) ^ ((d >> 4) & 7))) & 15) * 16 +
-           half * 8;
+// LDS layout of a transposed V tile.  Row d (one head_dim index) holds the tile's BN = 64
+// keys as 8 "units" of 16 bytes: unit (ks, hl) holds keys 16ks + 4hl + 0..3 (first 8 bytes) and
+// 16ks + 8 + 4hl + 0..3 (last 8 bytes), exactly the 8 keys, in register order, that lane half hl
+// of an MFMA needs at k-step ks of P V, so each V^T operand is one 128-bit read.  Units of one
+// k-step and one 32-row block of d form a 1 KiB region (4 lines of 8 rows x 2 units), padded
+// to RGS bytes; within a line, unit hl of row d sits at 16-byte slot
+// (2 (d % 8) + hl) ^ ((d / 8) % 4) ^ x(hl).  With 64 banks x 4 B:
+//   * an operand read (16 lanes: one unit of 16 consecutive rows) touches every bank once, and
+//     its address is one per-lane base plus the compile-time offset ks*KSS + block*RGS;
+//   * a staging write (32 lanes: column 8dq + jj of 16 column chunks dq, both halves; at d=64
+//     8 chunks x both lane halves) touches every bank once: the padding shifts the regions of
+//     consecutive 32-row blocks by 16 (d=128) or 32 (d=64) banks, and x(hl) = 4 hl at d=64
+//     moves the two lane halves to different slot quads.  The write addresses of one thread
+//     are two (d=128) or four (d=64) bases plus multiples of 64 bytes.
+template <int D>
+struct Vt {
+  static constexpr int RGS = D == 128 ? 1088 : 1152;
+  static constexpr int KSS = (D / 32) * RGS;  // one k-step: D/32 regions
+  static constexpr int BYTES = 4 * KSS;
+  __device__ static constexpr int x(int hl) { return D == 64 ? 4 * hl : 0; }
+  __device__ static constexpr int off(int d, int ks, int hl, int half) {
+    return ks * KSS + (d >> 5) * RGS + ((d >> 3) & 3) * 256 +
+           (((2 * (d & 7) + hl) ^ ((d >> 3) & 3) ^ x(hl)) * 16) + half * 8;
   }
 };
 
 typedef __attribute__((address_space(3))) void lds_void;
+
+// DMA of one 16-byte chunk per lane from a buffer resource into LDS: lane i writes dst + 16 i.
+// Compiled in the device pass only: with this builtin in a kernel body, the host pass of the
+// compiler omits the kernel's launch stub.
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, lds_void* dst, unsigned voff) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, 16, voff, 0, 0, 0);
+#endif
+}
 
 template <bool BF16, int D, int MODE>
 __global__ __launch_bounds__(kThreads, 2) void fa_fwd_kernel(Params p) {
@@ -201,7 +225,7 @@ __global__ __launch_bounds__(kThreads, 2) void fa_fwd_kernel(Params p) {
   constexpr int RPR = L::RPR, RS = L::RS;
   constexpr int NREG = BN / RPR;     // regions per tile
   constexpr int T_BYTES = NREG * RS; // one K tile (BN rows)
-  constexpr int VT_BYTES = D * 128;  // one transposed V tile (D rows of BN = 64 keys)
+  constexpr int VT_BYTES = Vt<D>::BYTES;  // one transposed V tile (D rows of BN = 64 keys)
   constexpr int NDQ = D / 8;         // 16-byte column chunks of a V row
   constexpr int VS_THREADS = 16 * NDQ;  // V staging: one key quad x one column chunk each
   constexpr int M_WORDS = MODE == kBitmask ? BM * NKB : 1;
@@ -290,19 +314,26 @@ __global__ __launch_bounds__(kThreads, 2) void fa_fwd_kernel(Params p) {
   }
   __syncthreads();
 
-  // ---- K/V staging by DMA: instruction i of this wave fills region n = i*NW + wave; lane = slot
-  // s holds chunk s / RPR of row n*RPR + ((s % RPR) ^ x(chunk)).
+  // Buffer resource over the K or V rows of this (batch, KV head) from key `key0` on.  Rows at
+  // or past S lie outside it: their reads return zeros and touch no memory, so a ragged last
+  // tile needs no address clamp.
+  const unsigned row_bytes = (unsigned)kv_stride * 2u;
+  auto rows_rsrc = [&](const uint16_t* base, int key0) __attribute__((always_inline)) {
+    const unsigned rows = (unsigned)max(S - key0, 0);
+    return __builtin_amdgcn_make_buffer_rsrc((void*)(base + (size_t)key0 * kv_stride), (short)0,
+                                             (int)(rows * row_bytes), 0x00020000);
+  };
+
+  // ---- K staging by DMA (buffer load into LDS): instruction i of this wave fills region
+  // n = i*NW + wave; lane = slot s holds chunk s / RPR of row n*RPR + ((s % RPR) ^ x(chunk)).
   const int dma_c = lane / RPR;
-  const int dma_rr = (lane % RPR) ^ L::x(dma_c);
+  const unsigned dma_off = (unsigned)((lane % RPR) ^ L::x(dma_c)) * row_bytes + dma_c * 16u;
   auto dma_tile = [&](const uint16_t* __restrict__ src, int j, unsigned char* dst)
                       __attribute__((always_inline)) {
-    const int k0 = j * BN;
 #pragma unroll
     for (int i = 0; i < DMA_PER_WAVE; ++i) {
       const int n = i * NW + wave;
-      const int key = min(k0 + n * RPR + dma_rr, S - 1);
-      __builtin_amdgcn_global_load_lds((const void*)(src + key * kv_stride + dma_c * 8),
-                                       (lds_void*)(dst + n * RS), 16, 0, 0);
+      dma16(rows_rsrc(src, j * BN + n * RPR), (lds_void*)(dst + n * RS), dma_off);
     }
   };
 
@@ -312,31 +343,36 @@ __global__ __launch_bounds__(kThreads, 2) void fa_fwd_kernel(Params p) {
   // q+2 (same V^T unit, other half) so the two 16-lane halves of a write never share a bank.
   // The four 16-byte pieces (one per key) are loaded into registers early, then transposed with
   // byte permutes into eight 8-byte pieces (one per column) and written at their V^T unit:
-  // unit 2(q/4) + (q%2), half (q/2)%2.
+  // unit (q/4, q%2), half (q/2)%2.
   const int vs_dq = D == 128 ? (tid & 15) : (tid & 7);
   const int vs_qi = D == 128 ? (tid >> 4) : (tid >> 3);
   const int vs_q = 4 * (vs_qi >> 2) + ((vs_qi >> 1) & 1) + 2 * (vs_qi & 1);
+  const bool vs_thread = VS_THREADS == NT || tid < VS_THREADS;
+  const unsigned vs_off = (unsigned)(4 * vs_q) * row_bytes + 16u * vs_dq;
   u32x4 vstage[4];
   auto v_load = [&](int j) __attribute__((always_inline)) {
-    if (tid < VS_THREADS) {
-      const int k0 = j * BN;
+    if (vs_thread) {
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        const int key = min(k0 + 4 * vs_q + kk, S - 1);
-        vstage[kk] = *(const u32x4*)(vg + key * kv_stride + 8 * vs_dq);
-      }
+      for (int kk = 0; kk < 4; ++kk)
+        vstage[kk] = __builtin_bit_cast(
+            u32x4, __builtin_amdgcn_raw_buffer_load_b128(rows_rsrc(vg, j * BN + kk), vs_off, 0, 0));
     }
   };
+  // V^T write addresses of this thread: column 8dq + jj at base jj % P plus 64 (jj / P) * P / 2.
+  constexpr int VP = D == 128 ? 2 : 4;
+  int vs_base[VP];
+#pragma unroll
+  for (int r = 0; r < VP; ++r)
+    vs_base[r] = Vt<D>::off(8 * vs_dq + r, vs_q >> 2, vs_q & 1, (vs_q >> 1) & 1);
   auto v_store = [&](unsigned char* vt) __attribute__((always_inline)) {
-    if (tid < VS_THREADS) {
-      const int u = 2 * (vs_q >> 2) + (vs_q & 1), half = (vs_q >> 1) & 1;
+    if (vs_thread) {
 #pragma unroll
       for (int jj = 0; jj < 8; ++jj) {
         const int m = jj >> 1;
         const u32 sel = (jj & 1) ? 0x07060302u : 0x05040100u;  // high / low 16-bit halves
         const u32x2 col = {__builtin_amdgcn_perm(vstage[1][m], vstage[0][m], sel),
                            __builtin_amdgcn_perm(vstage[3][m], vstage[2][m], sel)};
-        *(u32x2*)(vt + VtLds::off(8 * vs_dq + jj, u, half)) = col;
+        *(u32x2*)(vt + vs_base[jj % VP] + (jj - jj % VP) * 32) = col;
       }
     }
   };
@@ -408,58 +444,65 @@ __global__ __launch_bounds__(kThreads, 2) void fa_fwd_kernel(Params p) {
   float l_run = 0.f;     // this lane's partial row sum (its 16 keys of each 32-key block)
   const float c = p.c;
 
-  // V^T operand (A of O^T += V^T P^T): lane l reads head_dim row 32*db + l%32, unit 2ks + hl,
-  // at a per-block base XOR 32*ks.
-  int vt_base[NDB];
-#pragma unroll
-  for (int db = 0; db < NDB; ++db) vt_base[db] = VtLds::off(32 * db + l32, hl, 0);
+  // V^T operand (A of O^T += V^T P^T): lane l reads head_dim row 32*db + l%32, unit (ks, hl).
+  const int vt_base = Vt<D>::off(l32, 0, hl, 0);
   auto v_operand = [&](const unsigned char* vb, int ks, int db) __attribute__((always_inline)) {
-    return *(const u32x4*)(vb + (vt_base[db] ^ (32 * ks)));
+    return *(const u32x4*)(vb + vt_base + ks * Vt<D>::KSS + db * Vt<D>::RGS);
   };
 
-  // One tile's compute: S^T = K Q^T (operands read one k-step ahead), masked online softmax,
-  // O = alpha O + V^T P^T (branch-free rescale, P straight from registers; P slots 0..3 of lane
-  // half hl hold keys 16ks + 4hl + 0..3 and slots 4..7 keys 16ks + 8 + 4hl + 0..3, the key order
-  // of a V^T unit).
-  auto compute = [&](const Cls& cls, const unsigned char* kb, const unsigned char* vb)
-                     __attribute__((always_inline)) {
-    f32x16 sacc[NKB];
+  // ---- Tile pipeline.  Iteration j issues the loads of V_{j+1} (registers), the mask words of
+  // tile j+2 (registers) and K_{j+2} (DMA into LDS), then runs two phases:
+  //   1. S_{j+1} = K_{j+1} Q^T on the matrix cores while the vector units run the masked online
+  //      softmax of S_j (computed one iteration earlier), in one instruction stream that the
+  //      scheduler interleaves (a matrix instruction, an operand read, a few vector
+  //      instructions, repeated);
+  //   2. O = alpha O + V_j^T P_j^T, with the transpose and LDS write of V_{j+1} interleaved,
+  // and ends at the one workgroup barrier of the tile.  K is staged two tiles ahead, V and the
+  // mask words one; the keep words of tile j are carried in registers from iteration j-1, so
+  // the mask buffer of tile j can be refilled during iteration j.  Loads past the last tile
+  // re-read the last tile (in bounds, never used).
+
+  // S^T = K Q^T for one tile, each operand read one matrix instruction ahead.
+  auto qk = [&](const unsigned char* kb, f32x16 (&s)[NKB]) __attribute__((always_inline)) {
 #pragma unroll
     for (int kb32 = 0; kb32 < NKB; ++kb32)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) sacc[kb32][r] = 0.f;
-    u32x4 ka[2][NKB];
+      for (int r = 0; r < 16; ++r) s[kb32][r] = 0.f;
+    constexpr int N = QKS * NKB;
+    u32x4 ka[2];
+    ka[0] = *(const u32x4*)(kb + op_addr(0, 0));
 #pragma unroll
-    for (int kb32 = 0; kb32 < NKB; ++kb32) ka[0][kb32] = *(const u32x4*)(kb + op_addr(0, kb32));
-#pragma unroll
-    for (int ks = 0; ks < QKS; ++ks) {
-      if (ks + 1 < QKS) {
-#pragma unroll
-        for (int kb32 = 0; kb32 < NKB; ++kb32)
-          ka[(ks + 1) & 1][kb32] = *(const u32x4*)(kb + op_addr(ks + 1, kb32));
-      }
-#pragma unroll
-      for (int kb32 = 0; kb32 < NKB; ++kb32)
-        sacc[kb32] = mfma32<BF16>(ka[ks & 1][kb32], qreg[ks], sacc[kb32]);
+    for (int i = 0; i < N; ++i) {
+      if (i + 1 < N) ka[(i + 1) & 1] = *(const u32x4*)(kb + op_addr((i + 1) / NKB, (i + 1) % NKB));
+      s[i % NKB] = mfma32<BF16>(ka[i & 1], qreg[i / NKB], s[i % NKB]);
     }
+  };
 
-    if (!cls.full) {  // masked scores -> -inf: bit-field extract of the keep bit + bit-field insert
+  // Masked scores -> -inf (bit-field extract of the keep bit + bit-field insert), for tiles
+  // that are not full.  A tile with all-zero keep words becomes all -inf, whatever s held.
+  auto mask_scores = [&](const Cls& cls, f32x16 (&s)[NKB]) __attribute__((always_inline)) {
 #pragma unroll
-      for (int kb32 = 0; kb32 < NKB; ++kb32)
+    for (int kb32 = 0; kb32 < NKB; ++kb32)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int bit = 8 * (r >> 2) + (r & 3);
-          const int keep = ((int)(cls.wsh[kb32] << (31 - bit))) >> 31;
-          sacc[kb32][r] = __int_as_float((__float_as_int(sacc[kb32][r]) & keep) |
-                                         (~keep & (int)0xff800000));
-        }
-    }
+      for (int r = 0; r < 16; ++r) {
+        const int bit = 8 * (r >> 2) + (r & 3);
+        const int keep = ((int)(cls.wsh[kb32] << (31 - bit))) >> 31;
+        s[kb32][r] = __int_as_float((__float_as_int(s[kb32][r]) & keep) | (~keep & (int)0xff800000));
+      }
+  };
+
+  // Online softmax of one tile's (already masked) scores.  Updates m_run and l_run, writes P
+  // rounded to the input dtype into pk (slots 0..3 of lane half hl: keys 16ks + 4hl + 0..3,
+  // slots 4..7: keys 16ks + 8 + 4hl + 0..3, the key order of a V^T unit) and returns
+  // alpha = 2^(m_old - m_new).  An all -inf tile leaves m_run and l_run unchanged and gives
+  // alpha = 1 and P = 0 (m_run is finite).
+  auto softmax = [&](f32x16 (&s)[NKB], u32x4 (&pk)[PKS]) __attribute__((always_inline)) {
     // Row max: four independent in-lane chains of 3-input maxima (v_max3_f32) over 8 scores
     // each, then across the two lane halves.
     float mx4[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      const f32x16& v = sacc[(q >> 1) % NKB];
+      const f32x16& v = s[(q >> 1) % NKB];
       const int b0 = 8 * (q & 1);
       float m = __builtin_fmaxf(__builtin_fmaxf(v[b0], v[b0 + 1]), v[b0 + 2]);
       m = __builtin_fmaxf(__builtin_fmaxf(m, v[b0 + 3]), v[b0 + 4]);
@@ -473,7 +516,6 @@ __global__ __launch_bounds__(kThreads, 2) void fa_fwd_kernel(Params p) {
     m_run = m_new;
     // p = 2^(s*c - m), rounded to the input dtype; the row sum adds the rounded values
     // (v_dot2 against (1, 1)) so numerator and denominator see the same P.
-    u32x4 pk[PKS];
     float ps[2] = {0.f, 0.f};
 #pragma unroll
     for (int kb32 = 0; kb32 < NKB; ++kb32)
@@ -481,67 +523,111 @@ __global__ __launch_bounds__(kThreads, 2) void fa_fwd_kernel(Params p) {
       for (int h = 0; h < 2; ++h) {
         f32x8 t;
 #pragma unroll
-        for (int e = 0; e < 8; ++e)
-          t[e] = __builtin_amdgcn_exp2f(fmaf(sacc[kb32][8 * h + e], c, -m_new));
+        for (int e = 0; e < 8; ++e) t[e] = __builtin_amdgcn_exp2f(fmaf(s[kb32][8 * h + e], c, -m_new));
         const u32x4 pw = pack8<BF16>(t);
         pk[2 * kb32 + h] = pw;
 #pragma unroll
         for (int e = 0; e < 4; ++e) ps[e & 1] = dot2_ones<BF16>(pw[e], ps[e & 1]);
       }
     l_run = l_run * alpha + (ps[0] + ps[1]);
+    return alpha;
+  };
 
+  // O = alpha O + V^T P^T (branch-free rescale, P straight from registers), each V^T operand
+  // read one matrix instruction ahead; the V^T write of the next tile (`fill`) shares the
+  // instruction stream.
+  auto pv = [&](const unsigned char* vb, const u32x4 (&pk)[PKS], float alpha, unsigned char* fill)
+                __attribute__((always_inline)) {
+    constexpr int N = PKS * NDB;
+    u32x4 va[2];
+    va[0] = v_operand(vb, 0, 0);
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
       for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
-    u32x4 va[2][NDB];
 #pragma unroll
-    for (int db = 0; db < NDB; ++db) va[0][db] = v_operand(vb, 0, db);
+    for (int i = 0; i < N; ++i) {  // i = db * PKS + ks: one accumulator's k-steps back to back
+      const int db = i / PKS, ks = i % PKS;
+      if (i + 1 < N) va[(i + 1) & 1] = v_operand(vb, (i + 1) % PKS, (i + 1) / PKS);
+      oacc[db] = mfma32<BF16>(va[i & 1], pk[ks], oacc[db]);
+    }
+    v_store(fill);
+  };
+
+  // Scheduling pattern of phase 1: matrix instructions spread evenly through the softmax.
+  auto phase1_pattern = [&]() __attribute__((always_inline)) {
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // first K operand
 #pragma unroll
-    for (int ks = 0; ks < PKS; ++ks) {
-      if (ks + 1 < PKS) {
-#pragma unroll
-        for (int db = 0; db < NDB; ++db)
-          va[(ks + 1) & 1][db] = v_operand(vb, ks + 1, db);
-      }
-#pragma unroll
-      for (int db = 0; db < NDB; ++db) oacc[db] = mfma32<BF16>(va[ks & 1][db], pk[ks], oacc[db]);
+    for (int i = 0; i < QKS * NKB; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+      if (i + 1 < QKS * NKB) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // next K read
+      __builtin_amdgcn_sched_group_barrier(0x002, FA_P1_VALU, 0);  // vector work of the softmax
     }
   };
 
-  // One tile: prefetch tile j+1 (K by DMA, V and mask words into registers), compute tile j,
-  // then wait for this wave's loads, write V^T and the mask words and meet the other waves at
-  // the barrier.
-  auto tile = [&](int j, const unsigned char* k_cur, const unsigned char* v_cur,
-                  const u32* m_cur, unsigned char* k_fill, unsigned char* v_fill, u32* m_fill)
-                  __attribute__((always_inline)) {
-    const bool more = j + 1 < n_tiles;
-    if (more) {
-      dma_tile(kg, j + 1, k_fill);
-      v_load(j + 1);
-      mask_load(j + 1);
+  // A tile that is not computed (skipped by the ballot, past the last tile, or a wave with no
+  // valid rows) gets all-zero keep words: its softmax is then an exact no-op.
+  auto retire = [&](Cls& cl, bool live) __attribute__((always_inline)) {
+    if (!live) {
+      cl.full = false;
+#pragma unroll
+      for (int kb32 = 0; kb32 < NKB; ++kb32) cl.wsh[kb32] = 0u;
     }
-    const Cls cls = classify(j, m_cur);
-    if (wave_live && !cls.skip) compute(cls, k_cur, v_cur);
+  };
+
+  // One pipelined iteration (see above).  s_cur holds S_j, s_nxt receives S_{j+1}.
+  auto iter = [&](int j, Cls& cls_cur, bool& live_cur, f32x16 (&s_cur)[NKB],
+                  f32x16 (&s_nxt)[NKB], const unsigned char* k_nxt, unsigned char* k_fill,
+                  const unsigned char* v_cur, unsigned char* v_fill, const u32* m_nxt,
+                  u32* m_fill) __attribute__((always_inline)) {
+    const int j1 = min(j + 1, n_tiles - 1), j2 = min(j + 2, n_tiles - 1);
+    v_load(j1);
+    mask_load(j2);
+    dma_tile(kg, j2, k_fill);
+    Cls cls_nxt = classify(j1, m_nxt);
+    const bool live_nxt = wave_live && j + 1 < n_tiles && !cls_nxt.skip;
+    retire(cls_nxt, live_nxt);
+    if (!cls_cur.full) mask_scores(cls_cur, s_cur);
+    u32x4 pk[PKS];
+    float alpha;
+    if (live_nxt) {
+      qk(k_nxt, s_nxt);
+      alpha = softmax(s_cur, pk);
+      phase1_pattern();
+    } else {
+      alpha = softmax(s_cur, pk);
+    }
+    if (live_cur) pv(v_cur, pk, alpha, v_fill);
+    else v_store(v_fill);
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's DMA and loads have landed
-    if (more) {
-      v_store(v_fill);
-      mask_store(m_fill);
-    }
+    mask_store(m_fill);
     __syncthreads();
+    cls_cur = cls_nxt;
+    live_cur = live_nxt;
   };
 
-  // Prologue: tile 0.
-  dma_tile(kg, 0, k_lds0);
+  // Prologue: V_0, masks 0 and 1, K_0 and K_1 staged; S_0 computed.
   v_load(0);
   mask_load(0);
-  mask_store(m_lds0);
+  dma_tile(kg, 0, k_lds0);
   __builtin_amdgcn_s_waitcnt(0x0F70);
   v_store(v_lds0);
+  mask_store(m_lds0);
+  mask_load(min(1, n_tiles - 1));
+  dma_tile(kg, min(1, n_tiles - 1), k_lds1);
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+  mask_store(m_lds1);
   __syncthreads();
+  Cls cls_cur = classify(0, m_lds0);
+  bool live_cur = wave_live && !cls_cur.skip;
+  retire(cls_cur, live_cur);
+  f32x16 sA[NKB], sB[NKB];
+  if (live_cur) qk(k_lds0, sA);
+  __syncthreads();  // every wave has read K_0 before iteration 0 refills its buffer
   for (int j = 0; j < n_tiles; j += 2) {
-    tile(j, k_lds0, v_lds0, m_lds0, k_lds1, v_lds1, m_lds1);
-    if (j + 1 < n_tiles) tile(j + 1, k_lds1, v_lds1, m_lds1, k_lds0, v_lds0, m_lds0);
+    iter(j, cls_cur, live_cur, sA, sB, k_lds1, k_lds0, v_lds0, v_lds1, m_lds1, m_lds0);
+    if (j + 1 < n_tiles)
+      iter(j + 1, cls_cur, live_cur, sB, sA, k_lds0, k_lds1, v_lds1, v_lds0, m_lds0, m_lds1);
   }
 
   // ---- Epilogue: O / l (0 for a row with no kept key), rounded, 8-byte stores.

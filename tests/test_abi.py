@@ -92,3 +92,12 @@ def test_python_binding_refuses_cpu_tensors():
     q = torch.zeros(1, 8, 2, 64, dtype=torch.bfloat16)
     with pytest.raises(ValueError, match="GPU"):
         fa.fa_fwd(q, q, q)
+
+
+def test_kernel_launch_stubs_defined():
+    """Every kernel the library launches is defined in it: an undefined kernel symbol makes the
+    library fail to load on a GPU machine even though lazy binding lets it load here."""
+    _lib()
+    undef = subprocess.run(["nm", "-D", "--undefined-only", fa.lib_path()], capture_output=True,
+                           text=True, check=True).stdout
+    assert "fa_fwd_kernel" not in undef, [l for l in undef.splitlines() if "fa_fwd_kernel" in l]
