@@ -93,6 +93,12 @@ constexpr int kBN = 64;           // keys per tile
 #ifndef FA_P1_VALU
 #define FA_P1_VALU 8
 #endif
+#ifndef FA_QK_AHEAD
+#define FA_QK_AHEAD 3
+#endif
+#ifndef FA_PV_AHEAD
+#define FA_PV_AHEAD 3
+#endif
 
 template <bool BF16>
 __device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
@@ -377,29 +383,29 @@ __global__ __launch_bounds__(kThreads, 2) void fa_fwd_kernel(Params p) {
     }
   };
 
-  // Mask words (bitmask mode): thread t < BM stages the NKB words of row t for a tile.
-  u32 mreg[NKB];
+  // Mask words (bitmask mode): thread t stages word t / BM of row t % BM for a tile (NKB = 2
+  // words per row, so the BM x NKB words of a tile take one load per thread).  The row pointer
+  // is clamped to a valid row and the word index to the row length, so the load needs no
+  // branch; words of rows >= S or past the row end are then replaced by 0.
+  static_assert(MODE != kBitmask || BM * NKB == NT, "one mask word per thread and tile");
+  u32 mreg = 0u;
   const u32* mrow = nullptr;
   bool mrow_ok = false;
-  if (MODE == kBitmask && tid < BM) {
-    const int grow = row0 + tid, pos = grow / G, h = hk * G + (grow - pos * G);
+  const int m_row = tid % BM, m_word = tid / BM;
+  if (MODE == kBitmask) {
+    const int grow = row0 + m_row, pos = grow / G, h = hk * G + (grow - pos * G);
     mrow_ok = pos < S;
-    if (mrow_ok) mrow = p.mask + (((size_t)b * Hq + h) * S + pos) * (size_t)p.W;
+    mrow = p.mask + (((size_t)b * Hq + h) * S + min(pos, S - 1)) * (size_t)p.W;
   }
   auto mask_load = [&](int j) __attribute__((always_inline)) {
-    if (MODE == kBitmask && tid < BM) {
-#pragma unroll
-      for (int w = 0; w < NKB; ++w) {
-        const int word = j * NKB + w;
-        mreg[w] = (mrow_ok && word < p.W) ? mrow[word] : 0u;
-      }
+    if (MODE == kBitmask) {
+      const int word = j * NKB + m_word;
+      const u32 x = mrow[min(word, p.W - 1)];
+      mreg = (mrow_ok && word < p.W) ? x : 0u;
     }
   };
   auto mask_store = [&](u32* mb) __attribute__((always_inline)) {
-    if (MODE == kBitmask && tid < BM) {
-#pragma unroll
-      for (int w = 0; w < NKB; ++w) mb[tid * NKB + w] = mreg[w];
-    }
+    if (MODE == kBitmask) mb[m_row * NKB + m_word] = mreg;
   };
 
   // Tile class of tile j for this wave: full (no masking), skip (a 64-lane ballot finds no kept
@@ -462,19 +468,22 @@ __global__ __launch_bounds__(kThreads, 2) void fa_fwd_kernel(Params p) {
   // the mask buffer of tile j can be refilled during iteration j.  Loads past the last tile
   // re-read the last tile (in bounds, never used).
 
-  // S^T = K Q^T for one tile, each operand read one matrix instruction ahead.
+  // S^T = K Q^T for one tile, each operand read QA matrix instructions ahead.
+  constexpr int QA = FA_QK_AHEAD;
   auto qk = [&](const unsigned char* kb, f32x16 (&s)[NKB]) __attribute__((always_inline)) {
 #pragma unroll
     for (int kb32 = 0; kb32 < NKB; ++kb32)
 #pragma unroll
       for (int r = 0; r < 16; ++r) s[kb32][r] = 0.f;
     constexpr int N = QKS * NKB;
-    u32x4 ka[2];
-    ka[0] = *(const u32x4*)(kb + op_addr(0, 0));
+    u32x4 ka[QA + 1];
+#pragma unroll
+    for (int i = 0; i < QA; ++i) ka[i] = *(const u32x4*)(kb + op_addr(i / NKB, i % NKB));
 #pragma unroll
     for (int i = 0; i < N; ++i) {
-      if (i + 1 < N) ka[(i + 1) & 1] = *(const u32x4*)(kb + op_addr((i + 1) / NKB, (i + 1) % NKB));
-      s[i % NKB] = mfma32<BF16>(ka[i & 1], qreg[i / NKB], s[i % NKB]);
+      if (i + QA < N)
+        ka[(i + QA) % (QA + 1)] = *(const u32x4*)(kb + op_addr((i + QA) / NKB, (i + QA) % NKB));
+      s[i % NKB] = mfma32<BF16>(ka[i % (QA + 1)], qreg[i / NKB], s[i % NKB]);
     }
   };
 
@@ -534,33 +543,38 @@ __global__ __launch_bounds__(kThreads, 2) void fa_fwd_kernel(Params p) {
   };
 
   // O = alpha O + V^T P^T (branch-free rescale, P straight from registers), each V^T operand
-  // read one matrix instruction ahead; the V^T write of the next tile (`fill`) shares the
+  // read PA matrix instructions ahead; the V^T write of the next tile (`fill`) shares the
   // instruction stream.
+  constexpr int PA = FA_PV_AHEAD;
   auto pv = [&](const unsigned char* vb, const u32x4 (&pk)[PKS], float alpha, unsigned char* fill)
                 __attribute__((always_inline)) {
-    constexpr int N = PKS * NDB;
-    u32x4 va[2];
-    va[0] = v_operand(vb, 0, 0);
+    constexpr int N = PKS * NDB;  // i = db * PKS + ks: one accumulator's k-steps back to back
+    u32x4 va[PA + 1];
+#pragma unroll
+    for (int i = 0; i < PA; ++i) va[i] = v_operand(vb, i % PKS, i / PKS);
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
       for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
 #pragma unroll
-    for (int i = 0; i < N; ++i) {  // i = db * PKS + ks: one accumulator's k-steps back to back
-      const int db = i / PKS, ks = i % PKS;
-      if (i + 1 < N) va[(i + 1) & 1] = v_operand(vb, (i + 1) % PKS, (i + 1) / PKS);
-      oacc[db] = mfma32<BF16>(va[i & 1], pk[ks], oacc[db]);
+    for (int i = 0; i < N; ++i) {
+      if (i + PA < N) va[(i + PA) % (PA + 1)] = v_operand(vb, (i + PA) % PKS, (i + PA) / PKS);
+      oacc[i / PKS] = mfma32<BF16>(va[i % (PA + 1)], pk[i % PKS], oacc[i / PKS]);
     }
     v_store(fill);
   };
 
-  // Scheduling pattern of phase 1: matrix instructions spread evenly through the softmax.
+  // Scheduling pattern of phase 1: the tile's global loads and matrix instructions spread
+  // evenly through the softmax.
+  constexpr int NVMEM = (VS_THREADS == NT ? 4 : 0) + DMA_PER_WAVE + (MODE == kBitmask ? 1 : 0);
   auto phase1_pattern = [&]() __attribute__((always_inline)) {
-    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // first K operand
+    constexpr int N = QKS * NKB;
+    __builtin_amdgcn_sched_group_barrier(0x100, QA, 0);  // first K operands
 #pragma unroll
-    for (int i = 0; i < QKS * NKB; ++i) {
+    for (int i = 0; i < N; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-      if (i + 1 < QKS * NKB) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // next K read
+      if (i + QA < N) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // a later K operand
+      if (i < NVMEM) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // one global load
       __builtin_amdgcn_sched_group_barrier(0x002, FA_P1_VALU, 0);  // vector work of the softmax
     }
   };
@@ -581,9 +595,11 @@ __global__ __launch_bounds__(kThreads, 2) void fa_fwd_kernel(Params p) {
                   const unsigned char* v_cur, unsigned char* v_fill, const u32* m_nxt,
                   u32* m_fill) __attribute__((always_inline)) {
     const int j1 = min(j + 1, n_tiles - 1), j2 = min(j + 2, n_tiles - 1);
-    v_load(j1);
-    mask_load(j2);
-    dma_tile(kg, j2, k_fill);
+    auto issue_loads = [&]() __attribute__((always_inline)) {
+      v_load(j1);
+      mask_load(j2);
+      dma_tile(kg, j2, k_fill);
+    };
     Cls cls_nxt = classify(j1, m_nxt);
     const bool live_nxt = wave_live && j + 1 < n_tiles && !cls_nxt.skip;
     retire(cls_nxt, live_nxt);
@@ -591,11 +607,13 @@ __global__ __launch_bounds__(kThreads, 2) void fa_fwd_kernel(Params p) {
     u32x4 pk[PKS];
     float alpha;
     if (live_nxt) {
+      issue_loads();
       qk(k_nxt, s_nxt);
       alpha = softmax(s_cur, pk);
       phase1_pattern();
-    } else {
+    } else {  // (loads issued after the softmax here, so they are not hoisted out of the branches)
       alpha = softmax(s_cur, pk);
+      issue_loads();
     }
     if (live_cur) pv(v_cur, pk, alpha, v_fill);
     else v_store(v_fill);

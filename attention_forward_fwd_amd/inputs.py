@@ -60,6 +60,18 @@ def make_qkv(w: Workload):
     return q, k, v
 
 
+def make_qkv_device(w: Workload, device):
+    """Q, K, V of the same shapes and N(0,1) distribution drawn directly on `device` (seeded
+    device generator).  For timing runs at sizes where drawing on the CPU would be slow; the
+    values differ from make_qkv's."""
+    g = torch.Generator(device=device).manual_seed(w.seed)
+    dt = TORCH_DTYPE[w.dtype]
+    shape_q = (w.batch, w.seq_len, w.n_q_heads, w.head_dim)
+    shape_kv = (w.batch, w.seq_len, w.n_kv_heads, w.head_dim)
+    return tuple(torch.randn(sh, generator=g, device=device, dtype=torch.float32).to(dt)
+                 for sh in (shape_q, shape_kv, shape_kv))
+
+
 def make_bitmask(w: Workload, seed_offset: int = 7):
     """Random packed mask [B, Hq, S, ceil(S/32)] as int32 words (uint32 bit patterns).
 

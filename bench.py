@@ -5,7 +5,8 @@ One step = one fa_fwd launch over the whole workload (every row tile, every head
 batch), inputs already resident in device memory.  Default workload: non-causal MHA prefill,
 bf16, head dim 128, 16 heads, batch 4 x 8192 tokens (the 32768-token prefill grid of
 https://yetianai.com/news/16520, section "七天跑出的成绩单").  The causal variant of the same
-shape is timed alongside and reported under "also".
+shape and every other workload of the grid (other sequence lengths, GQA, the short random-mask
+cases) are timed alongside and reported under "also".
 
 Prints ONE JSON line.  FLOPs are counted dense, 4*B*Hq*S^2*d, half of that for causal.
 """
@@ -45,6 +46,53 @@ def time_launches(fn, steps, warmup):
     end.record(stream)
     torch.cuda.synchronize()
     return start.elapsed_time(end) / steps   # ms per launch, HIP events on the launch stream
+
+
+def alg_bytes(w):
+    """Q, K, V (and the mask words) read once, O written once."""
+    qo = 2 * w.batch * w.seq_len * w.n_q_heads * w.head_dim * 2
+    kv = 2 * w.batch * w.seq_len * w.n_kv_heads * w.head_dim * 2
+    mk = w.batch * w.n_q_heads * w.seq_len * ((w.seq_len + 31) // 32) * 4 if w.mode == "bitmask" else 0
+    return qo + kv + mk
+
+
+def time_grid(fa_fwd, inputs, dev, main, steps):
+    """Time every other workload of the grid once (inputs drawn on the device): the prefill
+    shapes causal and non-causal, the GQA groupings, and the short random-mask cases (the
+    latter with algorithmic HBM bytes per second, since they sit below the ridge point)."""
+    import torch
+    grid = []
+    for B, S in inputs.PREFILL_SHAPES:
+        for causal in (False, True):
+            grid.append(inputs.mha_prefill(B, S, causal))
+    for B, S in inputs.PREFILL_SHAPES:
+        for hkv in (4, 8):
+            for causal in (False, True):
+                grid.append(inputs.gqa_prefill(B, S, hkv, causal))
+    grid += [inputs.short_masked(512), inputs.short_masked(1000), inputs.tiny_masked()]
+    out = {}
+    for w in grid:
+        if (w.mode, w.batch, w.seq_len, w.n_q_heads, w.n_kv_heads) == (
+                main.mode, main.batch, main.seq_len, main.n_q_heads, main.n_kv_heads):
+            continue
+        q, k, v = inputs.make_qkv_device(w, dev)
+        mask = None
+        if w.mode == "bitmask":
+            mask = inputs.make_bitmask(w).to(dev)
+        o = torch.empty_like(q)
+        small = w.seq_len <= 1024
+        ms = time_launches(lambda: fa_fwd(q, k, v, mode=w.mode, scale=w.scale, mask=mask, out=o),
+                           steps * (20 if small else 1), 3)
+        f = flops(w.batch, w.n_q_heads, w.seq_len, w.head_dim, w.mode)
+        rec = {"ms": ms, "tflops": f / (ms * 1e-3) / 1e12,
+               "frac_of_peak": f / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
+        if small:
+            gbs = alg_bytes(w) / (ms * 1e-3) / 1e9
+            rec.update({"us": ms * 1e3, "alg_bytes": alg_bytes(w), "hbm_gbs": gbs,
+                        "frac_of_hbm": gbs / PEAK_HBM_GBS})
+        out[w.label] = rec
+        del q, k, v, o, mask
+    return out
 
 
 def cpu_baseline(w, q, k, v, o_gpu, budget_s):
@@ -95,7 +143,8 @@ def main():
     ap.add_argument("--seq-len", type=int, default=8192)
     ap.add_argument("--cpu-budget", type=float, default=12.0,
                     help="seconds of oracle work for the CPU baseline (0 = skip)")
-    ap.add_argument("--no-also", action="store_true", help="skip the causal companion timing")
+    ap.add_argument("--no-also", action="store_true",
+                    help="skip the timings of the rest of the grid (other shapes, causal, GQA, masked)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run a plain elementwise kernel (512 MiB read, 512 MiB written) three "
                          "times, so hardware byte counters can be scaled by a kernel of known traffic")
@@ -132,15 +181,9 @@ def main():
     tflops = f / (ms * 1e-3) / 1e12
     o_main = out.clone()
 
-    also = {}
-    if not args.no_also:
-        ms_c = time_launches(lambda: step("causal"), max(5, args.steps // 2), 3)
-        fc = flops(w.batch, w.n_q_heads, w.seq_len, w.head_dim, "causal")
-        also[f"causal B{w.batch} S{w.seq_len}"] = {
-            "tflops": fc / (ms_c * 1e-3) / 1e12, "ms": ms_c,
-            "frac_of_peak": fc / (ms_c * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
+    also = {} if args.no_also else time_grid(fa_fwd, inputs, dev, w, max(5, args.steps // 2))
 
-    bytes_alg = 4 * w.batch * w.seq_len * w.n_q_heads * w.head_dim * 2   # Q, K, V read + O written
+    bytes_alg = alg_bytes(w)   # Q, K, V read + O written
     # HBM bytes per launch measured with rocprofv3 byte counters (profiles/traffic.json); only
     # reported while the kernel source is the one the counters were taken on.
     traffic = None
