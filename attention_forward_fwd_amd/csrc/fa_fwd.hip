@@ -79,6 +79,7 @@ struct Params {
   int S, Hq, Hkv, G, W;
   int n_rt;   // row tiles per (batch, kv head)
   int n_wg;   // workgroups in the grid
+  int xsplit; // XCDs sharing one (batch, KV head) of causal row tiles, or 0
   float c;    // |scale| * log2(e), floored at 2^-100
   u32 qflip;  // 0x80008000 when scale < 0 (moves the sign onto Q exactly), else 0
 };
@@ -258,10 +259,18 @@ __global__ __launch_bounds__(kThreads, 2) void fa_fwd_kernel(Params p) {
 
   // XCD-aware remap: the hardware deals workgroup i to XCD i % 8.  Give XCD x the contiguous
   // logical range so that row tiles of one KV head (which read the same K/V) share an L2.
+  // Causal row tiles of a (batch, KV head) run longest first.  When one head's row tiles are
+  // shared by xsplit > 1 XCDs (a long sequence with few heads), its tiles are dealt round-robin
+  // among them instead, so that those XCDs get equal causal work.
   int wg = blockIdx.x;
   {
-    const int x = wg & 7, idx = wg >> 3, q8 = p.n_wg >> 3, r8 = p.n_wg & 7;
-    wg = x * q8 + min(x, r8) + idx;
+    const int x = wg & 7, idx = wg >> 3;
+    if (MODE == kCausal && p.xsplit > 1) {
+      wg = (x / p.xsplit) * p.n_rt + (x % p.xsplit) + p.xsplit * idx;
+    } else {
+      const int q8 = p.n_wg >> 3, r8 = p.n_wg & 7;
+      wg = x * q8 + min(x, r8) + idx;
+    }
   }
   const int bh = wg / p.n_rt;
   int rt = wg - bh * p.n_rt;
@@ -735,6 +744,10 @@ fa_status fa_fwd(fa_dtype dtype, fa_mask_mode mask_mode, int batch, int n_q_head
   p.W = (seq_len + 31) / 32;
   p.n_rt = (int)n_rt;
   p.n_wg = (int)n_wg;
+  // Causal balance across the 8 XCDs: when the grid is a multiple of 8 and one head's row tiles
+  // fill exactly k > 1 XCDs' shares, the kernel deals each head's tiles over its k XCDs.
+  p.xsplit = 0;
+  if (n_wg % 8 == 0 && n_rt % (n_wg / 8) == 0 && n_rt > n_wg / 8) p.xsplit = (int)(n_rt / (n_wg / 8));
   // exp(x) = 2^(x log2 e): fold log2(e) into the scale.  A zero scale becomes a tiny positive
   // one (2^-100): every 2^(s*c - m) is then 1 to fp32 precision, the uniform average the zero
   // scale defines, without 0 * inf on masked scores.

@@ -102,6 +102,19 @@ def test_head_groupings(Hq, Hkv, mode):
     check_full(q, k, v, mode, D ** -0.5, m, label)
 
 
+@pytest.mark.parametrize("B,S,Hq,Hkv", [(1, 512, 8, 1), (1, 1000, 4, 2), (1, 2048, 8, 1)])
+def test_causal_few_heads_split_over_xcds(B, S, Hq, Hkv):
+    # One head's causal row tiles span several XCD shares of the grid (64 x 8 = 512, 2 x 16 =
+    # 32 and 128 workgroups): the tiles of a head are then dealt over those XCDs.
+    q, k, v = _qkv(B, S, Hq, Hkv, 128, "bf16", seed=8100 + S)
+    label = f"causal xcd split B{B} S{S} H{Hq}/{Hkv}"
+    log(f"case {label}")
+    if S <= 1000:
+        check_full(q, k, v, "causal", 128 ** -0.5, None, label)
+    else:
+        check_sampled(q, k, v, "causal", 128 ** -0.5, None, label)
+
+
 @pytest.mark.parametrize("scale", [0.0, -0.125, 1.0, 2.5])
 @pytest.mark.parametrize("mode", ["none", "causal", "bitmask"])
 def test_scales(scale, mode):
