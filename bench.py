@@ -95,7 +95,7 @@ def time_grid(fa_fwd, inputs, dev, main, steps):
     return out
 
 
-def cpu_baseline(w, q, k, v, o_gpu, budget_s):
+def cpu_baseline(w, q, k, v, mask, o_gpu, budget_s):
     """Time the fp64 oracle on a bounded sample of the same workload (row blocks of one head
     at full key length, as many as fit in budget_s) and check the GPU rows it covers."""
     import numpy as np
@@ -114,7 +114,7 @@ def cpu_baseline(w, q, k, v, o_gpu, budget_s):
         r0 = int(rng.integers(0, max(1, S - 256)))
         rows = np.arange(r0, min(S, r0 + 256))
         t0 = time.perf_counter()
-        ref = oracle.attention_rows(q, k, v, w.mode, w.scale, None, rows=rows, heads=[h],
+        ref = oracle.attention_rows(q, k, v, w.mode, w.scale, mask, rows=rows, heads=[h],
                                     batches=[b])
         t_used += time.perf_counter() - t0
         got = o_gpu[b, rows[0]:rows[-1] + 1, h].float().cpu().numpy().astype(np.float64)
@@ -134,13 +134,32 @@ def cpu_baseline(w, q, k, v, o_gpu, budget_s):
     }
 
 
+WORKLOADS = ("mha", "gqa4", "gqa8", "short-masked", "tiny-masked")
+
+
+def pick_workload(inputs, name, batch, seq_len, causal):
+    if name == "mha":
+        return inputs.mha_prefill(batch, seq_len, causal)
+    if name in ("gqa4", "gqa8"):
+        return inputs.gqa_prefill(batch, seq_len, 4 if name == "gqa4" else 8, causal)
+    if name == "short-masked":
+        return inputs.short_masked(seq_len)
+    return inputs.tiny_masked()
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", choices=WORKLOADS, default="mha",
+                    help="timed workload: MHA or GQA prefill (bf16, d128; --batch, --seq-len, "
+                         "--causal), the short random-mask case (fp16, d64, B16 H16; --seq-len 512 "
+                         "or 1000) or the tiny masked case")
     ap.add_argument("--batch", type=int, default=4)
-    ap.add_argument("--seq-len", type=int, default=8192)
+    ap.add_argument("--seq-len", type=int, default=None,
+                    help="default 8192 for prefill, 512 for short-masked")
+    ap.add_argument("--causal", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0,
                     help="seconds of oracle work for the CPU baseline (0 = skip)")
     ap.add_argument("--no-also", action="store_true",
@@ -159,9 +178,12 @@ def main():
     from attention_forward_fwd_amd import fa_fwd, inputs
 
     dev = torch.device("cuda:0")
-    w = inputs.mha_prefill(args.batch, args.seq_len, causal=False)
+    seq_len = args.seq_len or (512 if args.workload == "short-masked" else 8192)
+    w = pick_workload(inputs, args.workload, args.batch, seq_len, args.causal)
     q, k, v = inputs.make_qkv(w)
     qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    mask = inputs.make_bitmask(w) if w.mode == "bitmask" else None
+    maskd = mask.to(dev) if mask is not None else None
     out = torch.empty_like(qd)
 
     if args.copy_calibration:
@@ -173,8 +195,8 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    def step(mode=w.mode):
-        fa_fwd(qd, kd, vd, mode=mode, scale=w.scale, out=out)
+    def step():
+        fa_fwd(qd, kd, vd, mode=w.mode, scale=w.scale, mask=maskd, out=out)
 
     ms = time_launches(step, args.steps, args.warmup)
     f = flops(w.batch, w.n_q_heads, w.seq_len, w.head_dim, w.mode)
@@ -183,7 +205,7 @@ def main():
 
     also = {} if args.no_also else time_grid(fa_fwd, inputs, dev, w, max(5, args.steps // 2))
 
-    bytes_alg = alg_bytes(w)   # Q, K, V read + O written
+    bytes_alg = alg_bytes(w)   # Q, K, V (and mask) read + O written
     # HBM bytes per launch measured with rocprofv3 byte counters (profiles/traffic.json); only
     # reported while the kernel source is the one the counters were taken on.
     traffic = None
@@ -194,7 +216,22 @@ def main():
         sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
         tr = json.load(open(tfile))
         if tr.get("kernel_source_sha256") == sha:
-            traffic = tr.get(f"{w.mode}:B{w.batch}:S{w.seq_len}:H{w.n_q_heads}:d{w.head_dim}")
+            traffic = tr.get("per_launch_bytes", {}).get(w.label)
+    dname = {"bf16": "bf16", "f16": "fp16"}[w.dtype]
+    kname = f"fa_fwd_kernel<{dname}, d{w.head_dim}, {w.mode}>"
+    if w.mode == "bitmask":
+        # Below the ridge point (short sequences, d=64): HBM is the roofline.
+        gbs = bytes_alg / (ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": gbs / PEAK_HBM_GBS, "traffic": traffic, "algorithmic_bytes": bytes_alg,
+                "kernel": kname, "tflops": tflops}
+    else:
+        roof = {"bound": "mfma", "achieved": tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": tflops / PEAK_BF16_TFLOPS, "traffic": traffic,
+                "algorithmic_bytes": bytes_alg, "kernel": kname}
+    desc = {"mha": "MHA prefill", "gqa4": "GQA prefill", "gqa8": "GQA prefill",
+            "short-masked": "short random-mask", "tiny-masked": "tiny random-mask"}[args.workload]
+    mode_desc = {"none": "non-causal", "causal": "causal", "bitmask": "bitmask"}[w.mode]
     rec = {
         "metric": METRIC,
         "value": tflops,
@@ -206,19 +243,17 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": w.dtype,
         "data": "synthetic",
-        "config": {"workload": f"non-causal MHA prefill bf16 d128 H16 B{w.batch} S{w.seq_len}",
+        "config": {"workload": f"{mode_desc} {desc} {w.dtype} d{w.head_dim} "
+                               f"H{w.n_q_heads}/{w.n_kv_heads} B{w.batch} S{w.seq_len}",
                    "batch": w.batch, "seq_len": w.seq_len, "n_q_heads": w.n_q_heads,
                    "n_kv_heads": w.n_kv_heads, "head_dim": w.head_dim, "mask_mode": w.mode},
-        "roofline": {"bound": "mfma", "achieved": tflops, "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": tflops / PEAK_BF16_TFLOPS, "traffic": traffic,
-                     "algorithmic_bytes": bytes_alg,
-                     "kernel": "fa_fwd_kernel<bf16, d128, none>"},
+        "roofline": roof,
         "also": also,
     }
     if args.cpu_budget > 0:
-        rec["cpu_baseline"] = cpu_baseline(w, q, k, v, o_main, args.cpu_budget)
+        rec["cpu_baseline"] = cpu_baseline(w, q, k, v, mask, o_main, args.cpu_budget)
     print(json.dumps(rec), flush=True)
 
 
