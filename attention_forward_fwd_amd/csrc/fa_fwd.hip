@@ -465,16 +465,18 @@ __global__ __launch_bounds__(kThreads, 2) void fa_fwd_kernel(Params p) {
     return *(const u32x4*)(vb + vt_base + ks * Vt<D>::KSS + db * Vt<D>::RGS);
   };
 
-  // ---- Tile pipeline.  Iteration j issues the loads of V_{j+1} (registers), the mask words of
-  // tile j+2 (registers) and K_{j+2} (DMA into LDS), then runs two phases:
+  // ---- Tile pipeline.  Iteration j writes V_{j+1}^T to LDS (from registers loaded one iteration
+  // earlier) and issues the loads of the mask words of tile j+2 (registers), K_{j+2} (DMA into
+  // LDS) and V_{j+2} (registers), then runs two phases:
   //   1. S_{j+1} = K_{j+1} Q^T on the matrix cores while the vector units run the masked online
   //      softmax of S_j (computed one iteration earlier), in one instruction stream that the
   //      scheduler interleaves (a matrix instruction, an operand read, a few vector
   //      instructions, repeated);
-  //   2. O = alpha O + V_j^T P_j^T, with the transpose and LDS write of V_{j+1} interleaved,
-  // and ends at the one workgroup barrier of the tile.  K is staged two tiles ahead, V and the
-  // mask words one; the keep words of tile j are carried in registers from iteration j-1, so
-  // the mask buffer of tile j can be refilled during iteration j.  Loads past the last tile
+  //   2. O = alpha O + V_j^T P_j^T,
+  // and ends at the one workgroup barrier of the tile.  K and V are loaded two tiles ahead (V
+  // lands in registers and is transposed into LDS one iteration later, in phase 1, off the
+  // barrier's path), the mask words one; the keep words of tile j are carried in registers
+  // from iteration j-1, so the mask buffer of tile j can be refilled during iteration j.  Loads past the last tile
   // re-read the last tile (in bounds, never used).
 
   // S^T = K Q^T for one tile, each operand read QA matrix instructions ahead.
@@ -552,10 +554,9 @@ __global__ __launch_bounds__(kThreads, 2) void fa_fwd_kernel(Params p) {
   };
 
   // O = alpha O + V^T P^T (branch-free rescale, P straight from registers), each V^T operand
-  // read PA matrix instructions ahead; the V^T write of the next tile (`fill`) shares the
-  // instruction stream.
+  // read PA matrix instructions ahead.
   constexpr int PA = FA_PV_AHEAD;
-  auto pv = [&](const unsigned char* vb, const u32x4 (&pk)[PKS], float alpha, unsigned char* fill)
+  auto pv = [&](const unsigned char* vb, const u32x4 (&pk)[PKS], float alpha)
                 __attribute__((always_inline)) {
     constexpr int N = PKS * NDB;  // i = db * PKS + ks: one accumulator's k-steps back to back
     u32x4 va[PA + 1];
@@ -570,7 +571,6 @@ __global__ __launch_bounds__(kThreads, 2) void fa_fwd_kernel(Params p) {
       if (i + PA < N) va[(i + PA) % (PA + 1)] = v_operand(vb, (i + PA) % PKS, (i + PA) / PKS);
       oacc[i / PKS] = mfma32<BF16>(va[i % (PA + 1)], pk[i % PKS], oacc[i / PKS]);
     }
-    v_store(fill);
   };
 
   // Scheduling pattern of phase 1: the tile's global loads and matrix instructions spread
@@ -584,6 +584,7 @@ __global__ __launch_bounds__(kThreads, 2) void fa_fwd_kernel(Params p) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
       if (i + QA < N) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // a later K operand
       if (i < NVMEM) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // one global load
+      if (i < 8) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);       // one V^T write
       __builtin_amdgcn_sched_group_barrier(0x002, FA_P1_VALU, 0);  // vector work of the softmax
     }
   };
@@ -605,9 +606,10 @@ __global__ __launch_bounds__(kThreads, 2) void fa_fwd_kernel(Params p) {
                   u32* m_fill) __attribute__((always_inline)) {
     const int j1 = min(j + 1, n_tiles - 1), j2 = min(j + 2, n_tiles - 1);
     auto issue_loads = [&]() __attribute__((always_inline)) {
-      v_load(j1);
       mask_load(j2);
       dma_tile(kg, j2, k_fill);
+      v_store(v_fill);  // V_{j+1}^T, from registers loaded during the previous iteration
+      v_load(j2);       // V_{j+2}: lands during this iteration, written in the next
     };
     Cls cls_nxt = classify(j1, m_nxt);
     const bool live_nxt = wave_live && j + 1 < n_tiles && !cls_nxt.skip;
@@ -624,16 +626,18 @@ __global__ __launch_bounds__(kThreads, 2) void fa_fwd_kernel(Params p) {
       alpha = softmax(s_cur, pk);
       issue_loads();
     }
-    if (live_cur) pv(v_cur, pk, alpha, v_fill);
-    else v_store(v_fill);
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's DMA and loads have landed
+    if (live_cur) pv(v_cur, pk, alpha);
+    // This wave's K DMA and mask words have landed (the V loads, issued last, may still be in
+    // flight: they are consumed in the next iteration).
+    if (vs_thread) __builtin_amdgcn_s_waitcnt(0x0F74);  // vmcnt(4)
+    else __builtin_amdgcn_s_waitcnt(0x0F70);            // vmcnt(0)
     mask_store(m_fill);
     __syncthreads();
     cls_cur = cls_nxt;
     live_cur = live_nxt;
   };
 
-  // Prologue: V_0, masks 0 and 1, K_0 and K_1 staged; S_0 computed.
+  // Prologue: V_0, masks 0 and 1, K_0 and K_1 staged, V_1 in registers; S_0 computed.
   v_load(0);
   mask_load(0);
   dma_tile(kg, 0, k_lds0);
@@ -642,6 +646,7 @@ __global__ __launch_bounds__(kThreads, 2) void fa_fwd_kernel(Params p) {
   mask_store(m_lds0);
   mask_load(min(1, n_tiles - 1));
   dma_tile(kg, min(1, n_tiles - 1), k_lds1);
+  v_load(min(1, n_tiles - 1));
   __builtin_amdgcn_s_waitcnt(0x0F70);
   mask_store(m_lds1);
   __syncthreads();
