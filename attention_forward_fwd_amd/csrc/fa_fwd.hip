@@ -51,6 +51,7 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <mutex>
 #include <type_traits>
 
 #include "fa.h"
@@ -75,8 +76,10 @@ struct Params {
   const uint16_t* k;
   const uint16_t* v;
   const u32* mask;
+  const uint16_t* vt;  // packed V^T tiles (see VtPack), when the kernel reads V that way
   uint16_t* o;
   int S, Hq, Hkv, G, W;
+  int n_kt;   // 64-key tiles per sequence
   int n_rt;   // row tiles per (batch, kv head)
   int n_wg;   // workgroups in the grid
   int xsplit; // XCDs sharing one (batch, KV head) of causal row tiles, or 0
@@ -91,6 +94,7 @@ constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * 64;
 constexpr int kBM = kWaves * 32;  // rows per workgroup
 constexpr int kBN = 64;           // keys per tile
+constexpr int kPackRowTiles = 8;  // row tiles per KV head from which V is packed once up front
 #ifndef FA_P1_VALU
 #define FA_P1_VALU 8
 #endif
@@ -214,14 +218,115 @@ typedef __attribute__((address_space(3))) void lds_void;
 // DMA of one 16-byte chunk per lane from a buffer resource into LDS: lane i writes dst + 16 i.
 // Compiled in the device pass only: with this builtin in a kernel body, the host pass of the
 // compiler omits the kernel's launch stub.
-__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, lds_void* dst, unsigned voff) {
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, lds_void* dst, unsigned voff,
+                                      unsigned soff = 0) {
 #if defined(__HIP_DEVICE_COMPILE__)
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, 16, voff, 0, 0, 0);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, 16, voff, soff, 0, 0);
 #endif
 }
 
-template <bool BF16, int D, int MODE>
+// Buffer resource over rows [key0, S) of a [S, row_elems]-strided tensor slice starting at
+// `base`: rows at or past S lie outside it, their reads return zeros and touch no memory.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const uint16_t* base, int key0, int S,
+                                                            int row_elems) {
+  const unsigned rows = (unsigned)max(S - key0, 0);
+  return __builtin_amdgcn_make_buffer_rsrc((void*)(base + (size_t)key0 * row_elems), (short)0,
+                                           (int)(rows * (unsigned)row_elems * 2u), 0x00020000);
+}
+
+// Per-thread V staging for one 64-key tile: thread t < THREADS owns column chunk dq (head_dim
+// 8dq..8dq+7) of key quad q (keys 4q..4q+3).  Consecutive lanes take consecutive column chunks
+// of one key row, so every load instruction reads whole rows.  Lanes 16-31 take quad q+2 (same
+// V^T unit, other half) so the two 16-lane halves of a write never share a bank.  The four
+// 16-byte pieces (one per key) are loaded into registers, then transposed with byte permutes
+// into eight 8-byte pieces (one per column) and written at their V^T unit: unit (q/4, q%2),
+// half (q/2)%2.
+template <int D>
+struct VStage {
+  static constexpr int THREADS = 16 * (D / 8);
+  static constexpr int VP = D == 128 ? 2 : 4;  // write address bases (see Vt)
+  bool active;
+  unsigned off;  // byte offset of this thread's first key row and column chunk
+  int base[VP];  // LDS offset of column 8dq + r, r < VP
+  __device__ VStage(int tid, unsigned row_bytes) {
+    const int dq = D == 128 ? (tid & 15) : (tid & 7);
+    const int qi = D == 128 ? (tid >> 4) : (tid >> 3);
+    const int q = 4 * (qi >> 2) + ((qi >> 1) & 1) + 2 * (qi & 1);
+    active = THREADS == 256 || tid < THREADS;
+    off = (unsigned)(4 * q) * row_bytes + 16u * dq;
+#pragma unroll
+    for (int r = 0; r < VP; ++r) base[r] = Vt<D>::off(8 * dq + r, q >> 2, q & 1, (q >> 1) & 1);
+  }
+  // Keys key0 + 4q + kk of the V slice at `v` (rows of row_elems elements, S valid rows).
+  __device__ __forceinline__ void load(u32x4 (&st)[4], const uint16_t* v, int key0, int S,
+                                       int row_elems) const {
+    if (active) {
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk)
+        st[kk] = __builtin_bit_cast(
+            u32x4, __builtin_amdgcn_raw_buffer_load_b128(rows_rsrc(v, key0 + kk, S, row_elems), off, 0, 0));
+    }
+  }
+  // Column 8dq + jj at base[jj % VP] + 32 (jj - jj % VP).
+  __device__ __forceinline__ void store(const u32x4 (&st)[4], unsigned char* vt) const {
+    if (active) {
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj) {
+        const int m = jj >> 1;
+        const u32 sel = (jj & 1) ? 0x07060302u : 0x05040100u;  // high / low 16-bit halves
+        const u32x2 col = {__builtin_amdgcn_perm(st[1][m], st[0][m], sel),
+                           __builtin_amdgcn_perm(st[3][m], st[2][m], sel)};
+        *(u32x2*)(vt + base[jj % VP] + (jj - jj % VP) * 32) = col;
+      }
+    }
+  }
+};
+
+// Packed V^T tiles in device memory, and their LDS image: for each (batch, KV head, 64-key
+// tile), 4 * D/32 regions of 1 KiB, region r = ks * D/32 + db for k-step ks and 32-row block db
+// of head_dim.  Slot t (16 bytes) of a region holds unit (ks, hl = t / 32) of row 32 db + t % 32
+// (the units of Vt).  An MFMA operand read of region r is then lane l -> slot l: 64 lanes read
+// 1 KiB of consecutive slots, which touches every LDS bank the same number of times whatever
+// the number of lanes served per cycle; and one DMA instruction copies one region (lane i ->
+// 16 i).
+template <int D>
+struct VtPack {
+  static constexpr int NREG = 4 * (D / 32);
+  static constexpr int TILE = NREG * 1024;
+};
+
+// Packs V [B, S, Hkv, D] into VtPack tiles: one workgroup per (batch, KV head, key tile), the
+// same register transpose as in-kernel staging, then a linear copy LDS -> memory.  Keys at or
+// past S are zeros.
+template <int D>
+__global__ __launch_bounds__(256) void vt_pack_kernel(const uint16_t* __restrict__ v,
+                                                      uint16_t* __restrict__ vt, int S, int Hkv,
+                                                      int n_kt) {
+  __shared__ __attribute__((aligned(1024))) unsigned char lds[Vt<D>::BYTES];
+  const int tid = threadIdx.x;
+  const int tile = blockIdx.x;
+  const int kt = tile % n_kt, bh = tile / n_kt, hk = bh % Hkv, b = bh / Hkv;
+  const int row_elems = Hkv * D;
+  const uint16_t* vg = v + ((size_t)b * S * Hkv + hk) * D;
+  const VStage<D> st(tid, (unsigned)row_elems * 2u);
+  u32x4 x[4];
+  st.load(x, vg, kt * 64, S, row_elems);
+  st.store(x, lds);
+  __syncthreads();
+  unsigned char* out = (unsigned char*)vt + (size_t)tile * VtPack<D>::TILE;
+#pragma unroll
+  for (int i = 0; i < VtPack<D>::TILE / 16 / 256; ++i) {
+    const int c = tid + 256 * i, r = c >> 6, t = c & 63;
+    const int ks = r / (D / 32), db = r % (D / 32);
+    *(u32x4*)(out + (size_t)c * 16) =
+        *(const u32x4*)(lds + Vt<D>::off(32 * db + (t & 31), ks, t >> 5, 0));
+  }
+}
+
+template <bool BF16, int D, int MODE, bool VPACK>
 __global__ __launch_bounds__(kThreads, 2) void fa_fwd_kernel(Params p) {
+  // VPACK: V arrives as packed V^T tiles (vt_pack_kernel) by DMA; otherwise each workgroup
+  // loads and transposes V itself.
   constexpr int BM = kBM, BN = kBN, NT = kThreads, NW = kWaves;
   constexpr int KC = D / 8;        // 16-byte chunks per row
   constexpr int NKB = BN / 32;     // 32-key blocks per tile (one MFMA output block each)
@@ -232,9 +337,8 @@ __global__ __launch_bounds__(kThreads, 2) void fa_fwd_kernel(Params p) {
   constexpr int RPR = L::RPR, RS = L::RS;
   constexpr int NREG = BN / RPR;     // regions per tile
   constexpr int T_BYTES = NREG * RS; // one K tile (BN rows)
-  constexpr int VT_BYTES = Vt<D>::BYTES;  // one transposed V tile (D rows of BN = 64 keys)
-  constexpr int NDQ = D / 8;         // 16-byte column chunks of a V row
-  constexpr int VS_THREADS = 16 * NDQ;  // V staging: one key quad x one column chunk each
+  constexpr int VT_BYTES = VPACK ? VtPack<D>::TILE : Vt<D>::BYTES;  // one transposed V tile
+  constexpr int VS_THREADS = VStage<D>::THREADS;  // V staging: one key quad x one column chunk each
   constexpr int M_WORDS = MODE == kBitmask ? BM * NKB : 1;
   constexpr int DMA_PER_WAVE = NREG / NW;             // one region per DMA instruction
   constexpr int QL = BM * KC / NT;                    // Q chunks staged per thread
@@ -329,15 +433,7 @@ __global__ __launch_bounds__(kThreads, 2) void fa_fwd_kernel(Params p) {
   }
   __syncthreads();
 
-  // Buffer resource over the K or V rows of this (batch, KV head) from key `key0` on.  Rows at
-  // or past S lie outside it: their reads return zeros and touch no memory, so a ragged last
-  // tile needs no address clamp.
   const unsigned row_bytes = (unsigned)kv_stride * 2u;
-  auto rows_rsrc = [&](const uint16_t* base, int key0) __attribute__((always_inline)) {
-    const unsigned rows = (unsigned)max(S - key0, 0);
-    return __builtin_amdgcn_make_buffer_rsrc((void*)(base + (size_t)key0 * kv_stride), (short)0,
-                                             (int)(rows * row_bytes), 0x00020000);
-  };
 
   // ---- K staging by DMA (buffer load into LDS): instruction i of this wave fills region
   // n = i*NW + wave; lane = slot s holds chunk s / RPR of row n*RPR + ((s % RPR) ^ x(chunk)).
@@ -348,46 +444,34 @@ __global__ __launch_bounds__(kThreads, 2) void fa_fwd_kernel(Params p) {
 #pragma unroll
     for (int i = 0; i < DMA_PER_WAVE; ++i) {
       const int n = i * NW + wave;
-      dma16(rows_rsrc(src, j * BN + n * RPR), (lds_void*)(dst + n * RS), dma_off);
+      dma16(rows_rsrc(src, j * BN + n * RPR, S, kv_stride), (lds_void*)(dst + n * RS), dma_off);
     }
   };
 
-  // ---- V staging (transposed).  Thread t < VS_THREADS owns column chunk dq (head_dim
-  // 8dq..8dq+7) of key quad q (keys 4q..4q+3).  Consecutive lanes take consecutive column
-  // chunks of one key row, so every load instruction reads whole rows.  Lanes 16-31 take quad
-  // q+2 (same V^T unit, other half) so the two 16-lane halves of a write never share a bank.
-  // The four 16-byte pieces (one per key) are loaded into registers early, then transposed with
-  // byte permutes into eight 8-byte pieces (one per column) and written at their V^T unit:
-  // unit (q/4, q%2), half (q/2)%2.
-  const int vs_dq = D == 128 ? (tid & 15) : (tid & 7);
-  const int vs_qi = D == 128 ? (tid >> 4) : (tid >> 3);
-  const int vs_q = 4 * (vs_qi >> 2) + ((vs_qi >> 1) & 1) + 2 * (vs_qi & 1);
-  const bool vs_thread = VS_THREADS == NT || tid < VS_THREADS;
-  const unsigned vs_off = (unsigned)(4 * vs_q) * row_bytes + 16u * vs_dq;
+  // ---- V staging.  VPACK: one DMA instruction per 1 KiB region of a packed V^T tile (lane i
+  // -> 16 i), instruction i of this wave taking region i*NW + wave.  Otherwise: loads into
+  // registers, transposed into LDS by VStage.
+  const VStage<D> vst(tid, row_bytes);
+  const bool vs_thread = !VPACK && vst.active;
   u32x4 vstage[4];
   auto v_load = [&](int j) __attribute__((always_inline)) {
-    if (vs_thread) {
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk)
-        vstage[kk] = __builtin_bit_cast(
-            u32x4, __builtin_amdgcn_raw_buffer_load_b128(rows_rsrc(vg, j * BN + kk), vs_off, 0, 0));
-    }
+    if (!VPACK) vst.load(vstage, vg, j * BN, S, kv_stride);
   };
-  // V^T write addresses of this thread: column 8dq + jj at base jj % P plus 64 (jj / P) * P / 2.
-  constexpr int VP = D == 128 ? 2 : 4;
-  int vs_base[VP];
-#pragma unroll
-  for (int r = 0; r < VP; ++r)
-    vs_base[r] = Vt<D>::off(8 * vs_dq + r, vs_q >> 2, vs_q & 1, (vs_q >> 1) & 1);
   auto v_store = [&](unsigned char* vt) __attribute__((always_inline)) {
-    if (vs_thread) {
+    if (!VPACK) vst.store(vstage, vt);
+  };
+  constexpr int VDMA_PER_WAVE = VtPack<D>::NREG / NW;
+  static_assert(VDMA_PER_WAVE * NW == VtPack<D>::NREG, "packed V^T regions split over waves");
+  const __amdgpu_buffer_rsrc_t vt_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(VPACK ? p.vt + (size_t)bh * p.n_kt * (VtPack<D>::TILE / 2) : p.v), (short)0,
+      VPACK ? p.n_kt * VtPack<D>::TILE : 0, 0x00020000);
+  auto v_dma = [&](int j, unsigned char* dst) __attribute__((always_inline)) {
+    if (VPACK) {
 #pragma unroll
-      for (int jj = 0; jj < 8; ++jj) {
-        const int m = jj >> 1;
-        const u32 sel = (jj & 1) ? 0x07060302u : 0x05040100u;  // high / low 16-bit halves
-        const u32x2 col = {__builtin_amdgcn_perm(vstage[1][m], vstage[0][m], sel),
-                           __builtin_amdgcn_perm(vstage[3][m], vstage[2][m], sel)};
-        *(u32x2*)(vt + vs_base[jj % VP] + (jj - jj % VP) * 32) = col;
+      for (int i = 0; i < VDMA_PER_WAVE; ++i) {
+        const int n = i * NW + wave;
+        dma16(vt_rsrc, (lds_void*)(dst + n * 1024), lane * 16u + n * 1024u,
+              (unsigned)(j * VtPack<D>::TILE));
       }
     }
   };
@@ -460,9 +544,11 @@ __global__ __launch_bounds__(kThreads, 2) void fa_fwd_kernel(Params p) {
   const float c = p.c;
 
   // V^T operand (A of O^T += V^T P^T): lane l reads head_dim row 32*db + l%32, unit (ks, hl).
-  const int vt_base = Vt<D>::off(l32, 0, hl, 0);
+  // (VPACK: region ks * D/32 + db, slot = lane.)
+  const int vt_base = VPACK ? lane * 16 : Vt<D>::off(l32, 0, hl, 0);
   auto v_operand = [&](const unsigned char* vb, int ks, int db) __attribute__((always_inline)) {
-    return *(const u32x4*)(vb + vt_base + ks * Vt<D>::KSS + db * Vt<D>::RGS);
+    if constexpr (VPACK) return *(const u32x4*)(vb + vt_base + (ks * (D / 32) + db) * 1024);
+    else return *(const u32x4*)(vb + vt_base + ks * Vt<D>::KSS + db * Vt<D>::RGS);
   };
 
   // ---- Tile pipeline.  Iteration j writes V_{j+1}^T to LDS (from registers loaded one iteration
@@ -575,7 +661,8 @@ __global__ __launch_bounds__(kThreads, 2) void fa_fwd_kernel(Params p) {
 
   // Scheduling pattern of phase 1: the tile's global loads and matrix instructions spread
   // evenly through the softmax.
-  constexpr int NVMEM = (VS_THREADS == NT ? 4 : 0) + DMA_PER_WAVE + (MODE == kBitmask ? 1 : 0);
+  constexpr int NVMEM = (VPACK ? VDMA_PER_WAVE : (VS_THREADS == NT ? 4 : 0)) + DMA_PER_WAVE +
+                        (MODE == kBitmask ? 1 : 0);
   auto phase1_pattern = [&]() __attribute__((always_inline)) {
     constexpr int N = QKS * NKB;
     __builtin_amdgcn_sched_group_barrier(0x100, QA, 0);  // first K operands
@@ -584,7 +671,7 @@ __global__ __launch_bounds__(kThreads, 2) void fa_fwd_kernel(Params p) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
       if (i + QA < N) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // a later K operand
       if (i < NVMEM) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // one global load
-      if (i < 8) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);       // one V^T write
+      if (!VPACK && i < 8) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);  // one V^T write
       __builtin_amdgcn_sched_group_barrier(0x002, FA_P1_VALU, 0);  // vector work of the softmax
     }
   };
@@ -608,8 +695,9 @@ __global__ __launch_bounds__(kThreads, 2) void fa_fwd_kernel(Params p) {
     auto issue_loads = [&]() __attribute__((always_inline)) {
       mask_load(j2);
       dma_tile(kg, j2, k_fill);
-      v_store(v_fill);  // V_{j+1}^T, from registers loaded during the previous iteration
-      v_load(j2);       // V_{j+2}: lands during this iteration, written in the next
+      v_dma(j1, v_fill);  // (VPACK) V_{j+1}^T straight into LDS
+      v_store(v_fill);    // V_{j+1}^T, from registers loaded during the previous iteration
+      v_load(j2);         // V_{j+2}: lands during this iteration, written in the next
     };
     Cls cls_nxt = classify(j1, m_nxt);
     const bool live_nxt = wave_live && j + 1 < n_tiles && !cls_nxt.skip;
@@ -630,7 +718,7 @@ __global__ __launch_bounds__(kThreads, 2) void fa_fwd_kernel(Params p) {
     // This wave's K DMA and mask words have landed (the V loads, issued last, may still be in
     // flight: they are consumed in the next iteration).
     if (vs_thread) __builtin_amdgcn_s_waitcnt(0x0F74);  // vmcnt(4)
-    else __builtin_amdgcn_s_waitcnt(0x0F70);            // vmcnt(0)
+    else __builtin_amdgcn_s_waitcnt(0x0F70);            // vmcnt(0) (VPACK: the V^T DMA too)
     mask_store(m_fill);
     __syncthreads();
     cls_cur = cls_nxt;
@@ -641,6 +729,7 @@ __global__ __launch_bounds__(kThreads, 2) void fa_fwd_kernel(Params p) {
   v_load(0);
   mask_load(0);
   dma_tile(kg, 0, k_lds0);
+  v_dma(0, v_lds0);
   __builtin_amdgcn_s_waitcnt(0x0F70);
   v_store(v_lds0);
   mask_store(m_lds0);
@@ -680,19 +769,62 @@ __global__ __launch_bounds__(kThreads, 2) void fa_fwd_kernel(Params p) {
 }
 
 template <bool BF16, int D, int MODE>
-hipError_t launch(const Params& p, hipStream_t s) {
+hipError_t launch(const Params& p, bool vpack, hipStream_t s) {
   void* args[] = {(void*)&p};
-  return hipLaunchKernel((const void*)fa_fwd_kernel<BF16, D, MODE>, dim3(p.n_wg),
-                         dim3(kThreads), args, 0, s);
+  const void* k = vpack ? (const void*)fa_fwd_kernel<BF16, D, MODE, true>
+                        : (const void*)fa_fwd_kernel<BF16, D, MODE, false>;
+  return hipLaunchKernel(k, dim3(p.n_wg), dim3(kThreads), args, 0, s);
 }
 
 template <bool BF16, int D>
-hipError_t launch_mode(int mode, const Params& p, hipStream_t s) {
+hipError_t launch_mode(int mode, const Params& p, bool vpack, hipStream_t s) {
   switch (mode) {
-    case kNone: return launch<BF16, D, kNone>(p, s);
-    case kCausal: return launch<BF16, D, kCausal>(p, s);
-    default: return launch<BF16, D, kBitmask>(p, s);
+    case kNone: return launch<BF16, D, kNone>(p, vpack, s);
+    case kCausal: return launch<BF16, D, kCausal>(p, vpack, s);
+    default: return launch<BF16, D, kBitmask>(p, vpack, s);
   }
+}
+
+template <int D>
+hipError_t launch_pack(const Params& p, int batch, hipStream_t s) {
+  const uint16_t* v = p.v;
+  uint16_t* vt = const_cast<uint16_t*>(p.vt);
+  int S = p.S, Hkv = p.Hkv, n_kt = p.n_kt;
+  void* args[] = {(void*)&v, (void*)&vt, (void*)&S, (void*)&Hkv, (void*)&n_kt};
+  return hipLaunchKernel((const void*)vt_pack_kernel<D>, dim3(batch * Hkv * n_kt), dim3(256), args,
+                         0, s);
+}
+
+// The packed V^T workspace comes from one memory pool per device, created on first use and
+// kept for the life of the process (memory freed back to it is retained for the next call).
+constexpr int kMaxDevices = 64;
+std::mutex g_pool_mutex;
+hipMemPool_t g_pools[kMaxDevices];
+
+hipError_t workspace_pool(hipMemPool_t* out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_pool_mutex);
+  if (!g_pools[dev]) {
+    hipMemPoolProps props = {};
+    props.allocType = hipMemAllocationTypePinned;
+    props.location.type = hipMemLocationTypeDevice;
+    props.location.id = dev;
+    hipMemPool_t pool;
+    e = hipMemPoolCreate(&pool, &props);
+    if (e != hipSuccess) return e;
+    uint64_t keep = UINT64_MAX;
+    e = hipMemPoolSetAttribute(pool, hipMemPoolAttrReleaseThreshold, &keep);
+    if (e != hipSuccess) {
+      (void)hipMemPoolDestroy(pool);
+      return e;
+    }
+    g_pools[dev] = pool;
+  }
+  *out = g_pools[dev];
+  return hipSuccess;
 }
 
 }  // namespace
@@ -749,6 +881,8 @@ fa_status fa_fwd(fa_dtype dtype, fa_mask_mode mask_mode, int batch, int n_q_head
   p.W = (seq_len + 31) / 32;
   p.n_rt = (int)n_rt;
   p.n_wg = (int)n_wg;
+  p.n_kt = (seq_len + kBN - 1) / kBN;
+  p.vt = nullptr;
   // Causal balance across the 8 XCDs: when the grid is a multiple of 8 and one head's row tiles
   // fill exactly k > 1 XCDs' shares, the kernel deals each head's tiles over its k XCDs.
   p.xsplit = 0;
@@ -761,12 +895,34 @@ fa_status fa_fwd(fa_dtype dtype, fa_mask_mode mask_mode, int batch, int n_q_head
   p.qflip = scale < 0.f ? 0x80008000u : 0u;
 
   hipStream_t s = (hipStream_t)stream;
-  const bool bf16 = dtype == FA_DTYPE_BF16;
-  hipError_t e;
-  if (bf16)
-    e = head_dim == 128 ? launch_mode<true, 128>(mask_mode, p, s) : launch_mode<true, 64>(mask_mode, p, s);
-  else
-    e = head_dim == 128 ? launch_mode<false, 128>(mask_mode, p, s) : launch_mode<false, 64>(mask_mode, p, s);
+  // Packed V^T (one pre-pass over V) when each KV head's V tiles would otherwise be transposed
+  // by kPackRowTiles or more row-tile workgroups; its offsets must stay 31-bit.
+  const int64_t tile_bytes = head_dim == 128 ? VtPack<128>::TILE : VtPack<64>::TILE;
+  const bool vpack = n_rt >= kPackRowTiles && (int64_t)p.n_kt * tile_bytes < ((int64_t)1 << 31);
+  hipError_t e = hipSuccess;
+  void* ws = nullptr;
+  if (vpack) {
+    hipMemPool_t pool;
+    e = workspace_pool(&pool);
+    if (e == hipSuccess)
+      e = hipMallocFromPoolAsync(&ws, (size_t)batch * n_kv_heads * p.n_kt * tile_bytes, pool, s);
+    if (e != hipSuccess) return FA_ERR_HIP;
+    p.vt = (const uint16_t*)ws;
+    e = head_dim == 128 ? launch_pack<128>(p, batch, s) : launch_pack<64>(p, batch, s);
+  }
+  if (e == hipSuccess) {
+    const bool bf16 = dtype == FA_DTYPE_BF16;
+    if (bf16)
+      e = head_dim == 128 ? launch_mode<true, 128>(mask_mode, p, vpack, s)
+                          : launch_mode<true, 64>(mask_mode, p, vpack, s);
+    else
+      e = head_dim == 128 ? launch_mode<false, 128>(mask_mode, p, vpack, s)
+                          : launch_mode<false, 64>(mask_mode, p, vpack, s);
+  }
+  if (ws) {
+    const hipError_t ef = hipFreeAsync(ws, s);
+    if (e == hipSuccess) e = ef;
+  }
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
