@@ -87,13 +87,15 @@ struct Params {
   u32 qflip;  // 0x80008000 when scale < 0 (moves the sign onto Q exactly), else 0
 };
 
-// Tile shape shared by every instance: 4 waves of 32 rows, 64 keys per tile; two workgroups
-// share a CU (two waves per SIMD, from different workgroups, so one wave's vector work can run
-// while the other's matrix work occupies the matrix cores).
-constexpr int kWaves = 4;
-constexpr int kThreads = kWaves * 64;
-constexpr int kBM = kWaves * 32;  // rows per workgroup
+// Tile shape: NW waves of 32 rows each per workgroup, 64 keys per tile, two waves per SIMD
+// either way: NW = 4 with two workgroups per CU (the two waves of a SIMD come from different
+// workgroups, so one wave's vector work runs while the other's matrix work occupies the matrix
+// cores), or NW = 8 with one workgroup per CU (each K and V tile staged in LDS then serves 256
+// rows: half the global->LDS traffic per FLOP), used when a KV head has many rows.
 constexpr int kBN = 64;           // keys per tile
+constexpr int kWide = 8;          // waves of the 256-row workgroup
+constexpr int kWideRows = 8192;   // rows per KV head (S x G) from which it is used
+constexpr int kWideRowsCausal = 16384;  // (causal: its longer tail pays off later)
 constexpr int kPackRowTiles = 8;  // row tiles per KV head from which V is packed once up front
 #ifndef FA_P1_VALU
 #define FA_P1_VALU 8
@@ -225,6 +227,22 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, lds_void* dst, u
 #endif
 }
 
+// s_waitcnt immediate: vmcnt(vm) with expcnt and lgkmcnt at `lgkm` (15 = no wait).
+constexpr int waitcnt_imm(int vm, int lgkm) {
+  return (vm & 15) | ((vm >> 4) << 14) | (7 << 4) | (lgkm << 8);
+}
+
+// Workgroup barrier of the tile pipeline.  The caller first waits (s_waitcnt) for exactly the
+// memory operations that other waves must see: its LDS writes and the global->LDS copies of
+// earlier iterations, while later copies stay in flight.  (__syncthreads would also wait for
+// those: its workgroup-scope fence drains every outstanding load that writes LDS.)  The empty
+// asm statements keep the compiler from moving memory accesses across the barrier.
+__device__ __forceinline__ void pipeline_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 // Buffer resource over rows [key0, S) of a [S, row_elems]-strided tensor slice starting at
 // `base`: rows at or past S lie outside it, their reads return zeros and touch no memory.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const uint16_t* base, int key0, int S,
@@ -241,7 +259,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const uint16_t* base
 // 16-byte pieces (one per key) are loaded into registers, then transposed with byte permutes
 // into eight 8-byte pieces (one per column) and written at their V^T unit: unit (q/4, q%2),
 // half (q/2)%2.
-template <int D>
+template <int D, int NT>
 struct VStage {
   static constexpr int THREADS = 16 * (D / 8);
   static constexpr int VP = D == 128 ? 2 : 4;  // write address bases (see Vt)
@@ -252,7 +270,7 @@ struct VStage {
     const int dq = D == 128 ? (tid & 15) : (tid & 7);
     const int qi = D == 128 ? (tid >> 4) : (tid >> 3);
     const int q = 4 * (qi >> 2) + ((qi >> 1) & 1) + 2 * (qi & 1);
-    active = THREADS == 256 || tid < THREADS;
+    active = THREADS >= NT || tid < THREADS;
     off = (unsigned)(4 * q) * row_bytes + 16u * dq;
 #pragma unroll
     for (int r = 0; r < VP; ++r) base[r] = Vt<D>::off(8 * dq + r, q >> 2, q & 1, (q >> 1) & 1);
@@ -308,7 +326,7 @@ __global__ __launch_bounds__(256) void vt_pack_kernel(const uint16_t* __restrict
   const int kt = tile % n_kt, bh = tile / n_kt, hk = bh % Hkv, b = bh / Hkv;
   const int row_elems = Hkv * D;
   const uint16_t* vg = v + ((size_t)b * S * Hkv + hk) * D;
-  const VStage<D> st(tid, (unsigned)row_elems * 2u);
+  const VStage<D, 256> st(tid, (unsigned)row_elems * 2u);
   u32x4 x[4];
   st.load(x, vg, kt * 64, S, row_elems);
   st.store(x, lds);
@@ -323,11 +341,12 @@ __global__ __launch_bounds__(256) void vt_pack_kernel(const uint16_t* __restrict
   }
 }
 
-template <bool BF16, int D, int MODE, bool VPACK>
-__global__ __launch_bounds__(kThreads, 2) void fa_fwd_kernel(Params p) {
+template <bool BF16, int D, int MODE, bool VPACK, int NW>
+__global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void fa_fwd_kernel(Params p) {
   // VPACK: V arrives as packed V^T tiles (vt_pack_kernel) by DMA; otherwise each workgroup
   // loads and transposes V itself.
-  constexpr int BM = kBM, BN = kBN, NT = kThreads, NW = kWaves;
+  constexpr int BM = NW * 32, BN = kBN, NT = NW * 64;
+  static_assert(NW == 4 || NW == 8, "workgroup shape");
   constexpr int KC = D / 8;        // 16-byte chunks per row
   constexpr int NKB = BN / 32;     // 32-key blocks per tile (one MFMA output block each)
   constexpr int QKS = D / 16;      // MFMA k-steps of Q K^T
@@ -338,12 +357,14 @@ __global__ __launch_bounds__(kThreads, 2) void fa_fwd_kernel(Params p) {
   constexpr int NREG = BN / RPR;     // regions per tile
   constexpr int T_BYTES = NREG * RS; // one K tile (BN rows)
   constexpr int VT_BYTES = VPACK ? VtPack<D>::TILE : Vt<D>::BYTES;  // one transposed V tile
-  constexpr int VS_THREADS = VStage<D>::THREADS;  // V staging: one key quad x one column chunk each
+  constexpr int VS_THREADS = VStage<D, NT>::THREADS;  // V staging: one key quad x one column chunk each
   constexpr int M_WORDS = MODE == kBitmask ? BM * NKB : 1;
   constexpr int DMA_PER_WAVE = NREG / NW;             // one region per DMA instruction
-  constexpr int QL = BM * KC / NT;                    // Q chunks staged per thread
-  static_assert(BM == 2 * BN, "Q staging uses the two K buffers, BN rows each");
-  static_assert(DMA_PER_WAVE * NW == NREG && QL * NT == BM * KC, "load split");
+  constexpr int QROWS = 2 * BN;                       // Q rows staged per pass (two K buffers)
+  constexpr int QPASS = BM / QROWS;                   // passes
+  constexpr int QL = QROWS * KC / NT;                 // Q chunks staged per thread and pass
+  static_assert(BM % QROWS == 0 && QL >= 1, "Q staging uses the two K buffers, BN rows each");
+  static_assert(DMA_PER_WAVE * NW == NREG && QL * NT == QROWS * KC, "load split");
   static_assert(BN == 64 && VS_THREADS <= NT, "V staging covers a 64-key tile");
 
   // Separate arrays (not one array indexed by buffer) so the compiler can tell the DMA into one
@@ -414,24 +435,29 @@ __global__ __launch_bounds__(kThreads, 2) void fa_fwd_kernel(Params p) {
     return op_base[ks & 1] + blk * BLK_OFF + (ks >> 1) * 2 * KS2_OFF;
   };
 
-  // ---- Q: coalesced 128-bit loads -> LDS (rows 0..63 in k_lds0, 64..127 in k_lds1) -> MFMA B
-  // operands held in registers for the whole key loop.
-#pragma unroll
-  for (int i = 0; i < QL; ++i) {
-    const int id = tid + NT * i, r = id / KC, c = id % KC;
-    const int grow = row0 + r, pos = grow / G, h = hk * G + (grow - pos * G);
-    u32x4 x = {0u, 0u, 0u, 0u};
-    if (pos < S) x = *(const u32x4*)(p.q + q_batch + ((size_t)pos * Hq + h) * D + c * 8);
-    *(u32x4*)((r < BN ? k_lds0 : k_lds1) + L::off(r % BN, c)) = x;
-  }
-  __syncthreads();
+  // ---- Q: coalesced 128-bit loads -> LDS (2 BN rows per pass: rows 0..63 of the pass in
+  // k_lds0, 64..127 in k_lds1) -> MFMA B operands held in registers for the whole key loop.
   u32x4 qreg[QKS];
 #pragma unroll
-  for (int ks = 0; ks < QKS; ++ks) {
-    const u32x4 x = *(const u32x4*)((wave < 2 ? k_lds0 : k_lds1) + op_addr(ks, wave & 1));
-    qreg[ks] = x ^ p.qflip;
+  for (int pass = 0; pass < QPASS; ++pass) {
+#pragma unroll
+    for (int i = 0; i < QL; ++i) {
+      const int id = tid + NT * i, r = id / KC, c = id % KC;
+      const int grow = row0 + pass * QROWS + r, pos = grow / G, h = hk * G + (grow - pos * G);
+      u32x4 x = {0u, 0u, 0u, 0u};
+      if (pos < S) x = *(const u32x4*)(p.q + q_batch + ((size_t)pos * Hq + h) * D + c * 8);
+      *(u32x4*)((r < BN ? k_lds0 : k_lds1) + L::off(r % BN, c)) = x;
+    }
+    __syncthreads();
+    if (wave / 4 == pass) {  // waves 4 pass .. 4 pass + 3 own these 128 rows
+#pragma unroll
+      for (int ks = 0; ks < QKS; ++ks) {
+        const u32x4 x = *(const u32x4*)(((wave & 3) < 2 ? k_lds0 : k_lds1) + op_addr(ks, wave & 1));
+        qreg[ks] = x ^ p.qflip;
+      }
+    }
+    __syncthreads();
   }
-  __syncthreads();
 
   const unsigned row_bytes = (unsigned)kv_stride * 2u;
 
@@ -451,7 +477,7 @@ __global__ __launch_bounds__(kThreads, 2) void fa_fwd_kernel(Params p) {
   // ---- V staging.  VPACK: one DMA instruction per 1 KiB region of a packed V^T tile (lane i
   // -> 16 i), instruction i of this wave taking region i*NW + wave.  Otherwise: loads into
   // registers, transposed into LDS by VStage.
-  const VStage<D> vst(tid, row_bytes);
+  const VStage<D, NT> vst(tid, row_bytes);
   const bool vs_thread = !VPACK && vst.active;
   u32x4 vstage[4];
   auto v_load = [&](int j) __attribute__((always_inline)) {
@@ -686,7 +712,8 @@ __global__ __launch_bounds__(kThreads, 2) void fa_fwd_kernel(Params p) {
     }
   };
 
-  // One pipelined iteration (see above).  s_cur holds S_j, s_nxt receives S_{j+1}.
+  // One pipelined iteration (see above).  s_cur holds S_j, s_nxt receives S_{j+1}; k_fill
+  // receives K_{j+2}, v_fill V_{j+1} (packed path) or V_{j+1}^T from registers.
   auto iter = [&](int j, Cls& cls_cur, bool& live_cur, f32x16 (&s_cur)[NKB],
                   f32x16 (&s_nxt)[NKB], const unsigned char* k_nxt, unsigned char* k_fill,
                   const unsigned char* v_cur, unsigned char* v_fill, const u32* m_nxt,
@@ -716,15 +743,21 @@ __global__ __launch_bounds__(kThreads, 2) void fa_fwd_kernel(Params p) {
     }
     if (live_cur) pv(v_cur, pk, alpha);
     // This wave's K DMA and mask words have landed (the V loads, issued last, may still be in
-    // flight: they are consumed in the next iteration).
-    if (vs_thread) __builtin_amdgcn_s_waitcnt(0x0F74);  // vmcnt(4)
-    else __builtin_amdgcn_s_waitcnt(0x0F70);            // vmcnt(0) (VPACK: the V^T DMA too)
+    // flight: they are consumed in the next iteration; on the packed path the V^T DMA has
+    // landed too).
+    if (vs_thread) __builtin_amdgcn_s_waitcnt(waitcnt_imm(4, 15));
+    else __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 15));
     mask_store(m_fill);
-    __syncthreads();
+    // This wave's LDS writes (mask words, V^T) are complete; then meet the other waves.
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm(63, 0));
+    pipeline_barrier();
     cls_cur = cls_nxt;
     live_cur = live_nxt;
   };
 
+  Cls cls_cur;
+  bool live_cur;
+  f32x16 sA[NKB], sB[NKB];
   // Prologue: V_0, masks 0 and 1, K_0 and K_1 staged, V_1 in registers; S_0 computed.
   v_load(0);
   mask_load(0);
@@ -739,10 +772,9 @@ __global__ __launch_bounds__(kThreads, 2) void fa_fwd_kernel(Params p) {
   __builtin_amdgcn_s_waitcnt(0x0F70);
   mask_store(m_lds1);
   __syncthreads();
-  Cls cls_cur = classify(0, m_lds0);
-  bool live_cur = wave_live && !cls_cur.skip;
+  cls_cur = classify(0, m_lds0);
+  live_cur = wave_live && !cls_cur.skip;
   retire(cls_cur, live_cur);
-  f32x16 sA[NKB], sB[NKB];
   if (live_cur) qk(k_lds0, sA);
   __syncthreads();  // every wave has read K_0 before iteration 0 refills its buffer
   for (int j = 0; j < n_tiles; j += 2) {
@@ -768,20 +800,23 @@ __global__ __launch_bounds__(kThreads, 2) void fa_fwd_kernel(Params p) {
   }
 }
 
+// Instances: 4 waves with or without packed V, 8 waves with packed V (a KV head with that many
+// rows always has enough row tiles to pack V).
 template <bool BF16, int D, int MODE>
-hipError_t launch(const Params& p, bool vpack, hipStream_t s) {
+hipError_t launch(const Params& p, bool vpack, int nw, hipStream_t s) {
   void* args[] = {(void*)&p};
-  const void* k = vpack ? (const void*)fa_fwd_kernel<BF16, D, MODE, true>
-                        : (const void*)fa_fwd_kernel<BF16, D, MODE, false>;
-  return hipLaunchKernel(k, dim3(p.n_wg), dim3(kThreads), args, 0, s);
+  const void* k = nw == kWide ? (const void*)fa_fwd_kernel<BF16, D, MODE, true, kWide>
+                  : vpack     ? (const void*)fa_fwd_kernel<BF16, D, MODE, true, 4>
+                              : (const void*)fa_fwd_kernel<BF16, D, MODE, false, 4>;
+  return hipLaunchKernel(k, dim3(p.n_wg), dim3(nw * 64), args, 0, s);
 }
 
 template <bool BF16, int D>
-hipError_t launch_mode(int mode, const Params& p, bool vpack, hipStream_t s) {
+hipError_t launch_mode(int mode, const Params& p, bool vpack, int nw, hipStream_t s) {
   switch (mode) {
-    case kNone: return launch<BF16, D, kNone>(p, vpack, s);
-    case kCausal: return launch<BF16, D, kCausal>(p, vpack, s);
-    default: return launch<BF16, D, kBitmask>(p, vpack, s);
+    case kNone: return launch<BF16, D, kNone>(p, vpack, nw, s);
+    case kCausal: return launch<BF16, D, kCausal>(p, vpack, nw, s);
+    default: return launch<BF16, D, kBitmask>(p, vpack, nw, s);
   }
 }
 
@@ -861,7 +896,13 @@ fa_status fa_fwd(fa_dtype dtype, fa_mask_mode mask_mode, int batch, int n_q_head
   if ((int64_t)seq_len * n_q_heads * head_dim >= ((int64_t)1 << 31)) return FA_ERR_BAD_SHAPE;
   const int G = n_q_heads / n_kv_heads;
   const int64_t rows = (int64_t)seq_len * G;
-  const int64_t n_rt = (rows + kBM - 1) / kBM;
+  // Packed V^T offsets must stay 31-bit.
+  const int n_kt = (seq_len + kBN - 1) / kBN;
+  const int64_t tile_bytes = head_dim == 128 ? VtPack<128>::TILE : VtPack<64>::TILE;
+  const bool pack_ok = (int64_t)n_kt * tile_bytes < ((int64_t)1 << 31);
+  const int nw =
+      pack_ok && rows >= (mask_mode == FA_MASK_CAUSAL ? kWideRowsCausal : kWideRows) ? kWide : 4;
+  const int64_t n_rt = (rows + nw * 32 - 1) / (nw * 32);
   const int64_t n_wg = n_rt * n_kv_heads * batch;
   if (n_wg >= ((int64_t)1 << 31)) return FA_ERR_BAD_SHAPE;
   if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o) & 15u) return FA_ERR_UNSUPPORTED;
@@ -881,7 +922,7 @@ fa_status fa_fwd(fa_dtype dtype, fa_mask_mode mask_mode, int batch, int n_q_head
   p.W = (seq_len + 31) / 32;
   p.n_rt = (int)n_rt;
   p.n_wg = (int)n_wg;
-  p.n_kt = (seq_len + kBN - 1) / kBN;
+  p.n_kt = n_kt;
   p.vt = nullptr;
   // Causal balance across the 8 XCDs: when the grid is a multiple of 8 and one head's row tiles
   // fill exactly k > 1 XCDs' shares, the kernel deals each head's tiles over its k XCDs.
@@ -896,9 +937,8 @@ fa_status fa_fwd(fa_dtype dtype, fa_mask_mode mask_mode, int batch, int n_q_head
 
   hipStream_t s = (hipStream_t)stream;
   // Packed V^T (one pre-pass over V) when each KV head's V tiles would otherwise be transposed
-  // by kPackRowTiles or more row-tile workgroups; its offsets must stay 31-bit.
-  const int64_t tile_bytes = head_dim == 128 ? VtPack<128>::TILE : VtPack<64>::TILE;
-  const bool vpack = n_rt >= kPackRowTiles && (int64_t)p.n_kt * tile_bytes < ((int64_t)1 << 31);
+  // by kPackRowTiles or more row-tile workgroups (always so for the 256-row workgroup).
+  const bool vpack = pack_ok && (nw == kWide || n_rt >= kPackRowTiles);
   hipError_t e = hipSuccess;
   void* ws = nullptr;
   if (vpack) {
@@ -913,11 +953,11 @@ fa_status fa_fwd(fa_dtype dtype, fa_mask_mode mask_mode, int batch, int n_q_head
   if (e == hipSuccess) {
     const bool bf16 = dtype == FA_DTYPE_BF16;
     if (bf16)
-      e = head_dim == 128 ? launch_mode<true, 128>(mask_mode, p, vpack, s)
-                          : launch_mode<true, 64>(mask_mode, p, vpack, s);
+      e = head_dim == 128 ? launch_mode<true, 128>(mask_mode, p, vpack, nw, s)
+                          : launch_mode<true, 64>(mask_mode, p, vpack, nw, s);
     else
-      e = head_dim == 128 ? launch_mode<false, 128>(mask_mode, p, vpack, s)
-                          : launch_mode<false, 64>(mask_mode, p, vpack, s);
+      e = head_dim == 128 ? launch_mode<false, 128>(mask_mode, p, vpack, nw, s)
+                          : launch_mode<false, 64>(mask_mode, p, vpack, nw, s);
   }
   if (ws) {
     const hipError_t ef = hipFreeAsync(ws, s);

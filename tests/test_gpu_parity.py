@@ -115,6 +115,23 @@ def test_causal_few_heads_split_over_xcds(B, S, Hq, Hkv):
         check_sampled(q, k, v, "causal", 128 ** -0.5, None, label)
 
 
+@pytest.mark.parametrize("S,Hq,Hkv,mode,D,dtype", [
+    (1500, 4, 4, "none", 128, "bf16"),      # 1500 rows per KV head: 128-row tiles, packed V
+    (1100, 16, 2, "none", 128, "bf16"),     # 8800 rows: 256-row workgroups
+    (2100, 16, 2, "causal", 128, "bf16"),   # 16800 rows: 256-row workgroups, causal
+    (1030, 8, 1, "bitmask", 64, "f16"),     # 8240 rows: 256-row workgroups, bitmask
+    (1030, 8, 1, "bitmask", 128, "bf16"),
+])
+def test_workgroup_shapes_ragged(S, Hq, Hkv, mode, D, dtype):
+    # Ragged lengths (not a multiple of 64) on each workgroup shape the library picks from the
+    # number of rows per KV head (sequence length x group size).
+    q, k, v = _qkv(1, S, Hq, Hkv, D, dtype, seed=8200 + S + Hq)
+    m = _mask(1, Hq, S, 8300 + S) if mode == "bitmask" else None
+    label = f"shape {mode} S{S} H{Hq}/{Hkv} d{D} {dtype}"
+    log(f"case {label}")
+    check_full(q, k, v, mode, D ** -0.5, m, label)
+
+
 @pytest.mark.parametrize("scale", [0.0, -0.125, 1.0, 2.5])
 @pytest.mark.parametrize("mode", ["none", "causal", "bitmask"])
 def test_scales(scale, mode):
