@@ -18,25 +18,27 @@
 //            keys are never kept.
 //
 // Design for gfx950 (what differs from the pages' NVIDIA kernels is deliberate):
-//   * Work: one workgroup = 4 waves x 32 rows.  A "row" is a (position, query head) pair; the
+//   * Work: one workgroup = 4 or 8 waves x 32 rows (8 when a KV head has many rows: each K/V
+//     tile staged in LDS then serves 256 rows).  A "row" is a (position, query head) pair; the
 //     rows of one KV head are ordered position-major, head-minor (row r -> position r / G,
 //     head hk*G + r % G), so a workgroup covers every query head of a GQA group at the same
-//     positions and each K/V tile staged in LDS feeds G heads.
+//     positions and each K/V tile staged in LDS feeds G heads.  Two waves per SIMD either way.
 //   * Matrix cores: v_mfma_f32_32x32x16_{bf16,f16}.  S^T = K Q^T puts one query in each lane
 //     column (lane l holds query l%32 and 16 keys per 32-key block), so the row max and row sum
 //     are in-lane reductions plus one v_permlane32_swap, and the rescale of O^T += V^T P^T
 //     touches only the lane's own query.  P never leaves registers: the S^T accumulator layout
 //     is re-used directly as the B operand of the P V product (keys permuted consistently on
 //     both operands).
-//   * LDS: K tiles are copied global -> LDS by the DMA path (global_load_lds_dwordx4, no
-//     registers) into 1 KiB regions of whole rows, padded so the 128-bit operand reads are
-//     conflict-free (layout below).  V tiles are read with coalesced 128-bit loads into
-//     registers one tile ahead, transposed in registers with byte permutes and written as V^T
-//     in a layout where every P V operand (8 keys of one head_dim column, in the key order of
-//     the P registers) is a single 128-bit read.  Q is staged once through the same LDS.  K, V
-//     and mask tiles are double-buffered, one workgroup barrier per tile.  Key rows past the
-//     sequence end are loaded from the last valid row (address clamp) and masked, so their
-//     probabilities are exactly 0.
+//   * Pipeline: per 64-key tile, one instruction stream computes S_{j+1} = K_{j+1} Q^T on the
+//     matrix cores while the vector units run the softmax of S_j, then O += V_j^T P_j^T; loads
+//     are spread through the first phase; one workgroup barrier per tile.
+//   * Memory: K tiles go global -> LDS by buffer-load DMA (no registers) into 1 KiB regions of
+//     whole rows, padded so the 128-bit operand reads are conflict-free.  V^T tiles (8 keys of
+//     one head_dim column per 128-bit operand, in the key order of the P registers) either come
+//     the same way from V packed once per call by vt_pack_kernel, or, for short sequences, are
+//     transposed by each workgroup (loads into registers two tiles ahead, byte permutes, LDS
+//     writes).  Buffer resources end at the sequence: key rows past it read as zeros and are
+//     masked, so their probabilities are exactly 0.  Q is staged once through LDS into registers.
 //   * Softmax: exp2 with log2(e) folded into the scale, running max floored at -1e30 so a
 //     fully masked row never makes NaN, unconditional (branch-free) rescale of O and l every
 //     tile, masked scores set to -inf with one bit-field extract and one bit-field insert.
@@ -876,7 +878,7 @@ const char* fa_status_string(int s) {
     case FA_ERR_UNSUPPORTED: return "unsupported dtype or head_dim, or misaligned pointer";
     case FA_ERR_BAD_MASK_MODE: return "unknown mask mode, or bitmask mode without a mask";
     case FA_ERR_BAD_SCALE: return "scale is not finite";
-    case FA_ERR_HIP: return "HIP runtime rejected the kernel launch";
+    case FA_ERR_HIP: return "HIP runtime rejected a kernel launch or the workspace allocation";
     default: return "unknown status";
   }
 }

@@ -32,14 +32,22 @@
  * Results are bitwise deterministic for a given input and device.
  *
  * Ownership and threading: every pointer is a DEVICE pointer owned by the caller, 16-byte
- * aligned (mask: 4-byte aligned).  The library allocates nothing, keeps no state, never
- * synchronises, and enqueues one kernel on `stream` (a hipStream_t; NULL = default stream).
- * o must not alias q, k, v or mask.  Calls are safe from several host threads.
+ * aligned (mask: 4-byte aligned).  o must not alias q, k, v or mask.  The call never
+ * synchronises; its work is enqueued on `stream` (a hipStream_t; NULL = default stream):
+ *   - when a KV head has more than 896 rows (seq_len x n_q_heads / n_kv_heads), two kernels: a
+ *     pre-pass that packs V into transposed tiles in a temporary device buffer (batch x
+ *     n_kv_heads x ceil(seq_len / 64) x 64 x head_dim x 2 bytes, about the size of V), then the
+ *     attention kernel.  The buffer is allocated and freed stream-ordered on `stream`
+ *     (hipMallocFromPoolAsync / hipFreeAsync) from a memory pool the library creates on first
+ *     use on each device and keeps until the process ends (memory freed to it is retained);
+ *   - otherwise the attention kernel alone.
+ * The library keeps no other state.  Calls are safe from several host threads.
  *
  * Errors: arguments are validated first, synchronously, with no HIP call; on error nothing is
- * enqueued and o is untouched.  After the launch, a launch error reported by HIP returns
- * FA_ERR_HIP.  Faults during execution surface at the caller's next synchronisation, as for any
- * HIP kernel.  Nothing is printed and no C++ exception crosses this interface.
+ * enqueued and o is untouched.  A failed workspace allocation or a launch error reported by
+ * HIP returns FA_ERR_HIP (after an allocation failure nothing is enqueued).  Faults during
+ * execution surface at the caller's next synchronisation, as for any HIP kernel.  Nothing is
+ * printed and no C++ exception crosses this interface.
  */
 #ifndef FA_H_
 #define FA_H_
@@ -68,10 +76,10 @@ typedef enum {
   FA_ERR_UNSUPPORTED = 3,   /* head_dim not 64 or 128, unknown dtype, misaligned pointer */
   FA_ERR_BAD_MASK_MODE = 4, /* unknown mask_mode, or FA_MASK_BITMASK with mask == NULL */
   FA_ERR_BAD_SCALE = 5,     /* scale is NaN or infinite */
-  FA_ERR_HIP = 6            /* the HIP runtime rejected the launch */
+  FA_ERR_HIP = 6            /* the HIP runtime rejected a launch or the workspace allocation */
 } fa_status;
 
-/* Forward attention (see the definition above).  Returns FA_OK once the kernel is enqueued. */
+/* Forward attention (see the definition above).  Returns FA_OK once its work is enqueued. */
 fa_status fa_fwd(fa_dtype dtype, fa_mask_mode mask_mode, int batch, int n_q_heads,
                  int n_kv_heads, int seq_len, int head_dim, float scale, const void* q,
                  const void* k, const void* v, const uint32_t* mask, void* o, void* stream);
