@@ -373,8 +373,10 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void fa_fwd_kernel(Params
   // buffer from LDS reads of another and does not wait for the DMA before those reads.
   __shared__ __attribute__((aligned(1024))) unsigned char k_lds0[T_BYTES];
   __shared__ __attribute__((aligned(1024))) unsigned char k_lds1[T_BYTES];
-  __shared__ __attribute__((aligned(1024))) unsigned char v_lds0[VT_BYTES];  // V^T tiles
-  __shared__ __attribute__((aligned(1024))) unsigned char v_lds1[VT_BYTES];
+  // V^T tiles (also the Q staging area, hence at least one K tile's size)
+  constexpr int VBUF_BYTES = VT_BYTES > T_BYTES ? VT_BYTES : T_BYTES;
+  __shared__ __attribute__((aligned(1024))) unsigned char v_lds0[VBUF_BYTES];
+  __shared__ __attribute__((aligned(1024))) unsigned char v_lds1[VBUF_BYTES];
   __shared__ __attribute__((aligned(16))) u32 m_lds0[M_WORDS];
   __shared__ __attribute__((aligned(16))) u32 m_lds1[M_WORDS];
 
@@ -437,29 +439,19 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void fa_fwd_kernel(Params
     return op_base[ks & 1] + blk * BLK_OFF + (ks >> 1) * 2 * KS2_OFF;
   };
 
-  // ---- Q: coalesced 128-bit loads -> LDS (2 BN rows per pass: rows 0..63 of the pass in
-  // k_lds0, 64..127 in k_lds1) -> MFMA B operands held in registers for the whole key loop.
+  // ---- Q: coalesced 128-bit loads -> LDS (2 BN rows per pass, through the two V^T buffers:
+  // rows 0..63 of the pass in v_lds0, 64..127 in v_lds1, K layout) -> MFMA B operands held in
+  // registers for the whole key loop.  Staged in the prologue below.
   u32x4 qreg[QKS];
-#pragma unroll
-  for (int pass = 0; pass < QPASS; ++pass) {
+  auto q_load = [&](int pass, u32x4 (&qx)[QL]) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < QL; ++i) {
       const int id = tid + NT * i, r = id / KC, c = id % KC;
       const int grow = row0 + pass * QROWS + r, pos = grow / G, h = hk * G + (grow - pos * G);
-      u32x4 x = {0u, 0u, 0u, 0u};
-      if (pos < S) x = *(const u32x4*)(p.q + q_batch + ((size_t)pos * Hq + h) * D + c * 8);
-      *(u32x4*)((r < BN ? k_lds0 : k_lds1) + L::off(r % BN, c)) = x;
+      qx[i] = (u32x4){0u, 0u, 0u, 0u};
+      if (pos < S) qx[i] = *(const u32x4*)(p.q + q_batch + ((size_t)pos * Hq + h) * D + c * 8);
     }
-    __syncthreads();
-    if (wave / 4 == pass) {  // waves 4 pass .. 4 pass + 3 own these 128 rows
-#pragma unroll
-      for (int ks = 0; ks < QKS; ++ks) {
-        const u32x4 x = *(const u32x4*)(((wave & 3) < 2 ? k_lds0 : k_lds1) + op_addr(ks, wave & 1));
-        qreg[ks] = x ^ p.qflip;
-      }
-    }
-    __syncthreads();
-  }
+  };
 
   const unsigned row_bytes = (unsigned)kv_stride * 2u;
 
@@ -509,7 +501,9 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void fa_fwd_kernel(Params
   // is clamped to a valid row and the word index to the row length, so the load needs no
   // branch; words of rows >= S or past the row end are then replaced by 0.
   static_assert(MODE != kBitmask || BM * NKB == NT, "one mask word per thread and tile");
-  u32 mreg = 0u;
+  u32 mreg = 0u;      // the loaded word ...
+  bool mvalid = false;  // ... and whether it is a real word of a valid row (applied at the store,
+                        // so no wait for the load is forced where it is issued)
   const u32* mrow = nullptr;
   bool mrow_ok = false;
   const int m_row = tid % BM, m_word = tid / BM;
@@ -521,12 +515,12 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void fa_fwd_kernel(Params
   auto mask_load = [&](int j) __attribute__((always_inline)) {
     if (MODE == kBitmask) {
       const int word = j * NKB + m_word;
-      const u32 x = mrow[min(word, p.W - 1)];
-      mreg = (mrow_ok && word < p.W) ? x : 0u;
+      mreg = mrow[min(word, p.W - 1)];
+      mvalid = mrow_ok && word < p.W;
     }
   };
   auto mask_store = [&](u32* mb) __attribute__((always_inline)) {
-    if (MODE == kBitmask) mb[m_row * NKB + m_word] = mreg;
+    if (MODE == kBitmask) mb[m_row * NKB + m_word] = mvalid ? mreg : 0u;
   };
 
   // Tile class of tile j for this wave: full (no masking), skip (a 64-lane ballot finds no kept
@@ -760,16 +754,51 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void fa_fwd_kernel(Params
   Cls cls_cur;
   bool live_cur;
   f32x16 sA[NKB], sB[NKB];
-  // Prologue: V_0, masks 0 and 1, K_0 and K_1 staged, V_1 in registers; S_0 computed.
-  v_load(0);
-  mask_load(0);
-  dma_tile(kg, 0, k_lds0);
+  // Prologue: Q in registers; V_0, masks 0 and 1, K_0 and K_1 staged, V_1 in registers; S_0
+  // computed.  The K_0 / K_1 DMA and the first V and mask loads are issued right behind the
+  // first Q loads, so their latency overlaps the Q staging; the staging barriers wait only for
+  // the Q loads and LDS accesses (not for those DMAs).
+  {
+    u32x4 qx[QL];
+    q_load(0, qx);
+    dma_tile(kg, 0, k_lds0);
+    dma_tile(kg, min(1, n_tiles - 1), k_lds1);
+    v_load(0);
+    mask_load(0);
+#pragma unroll
+    for (int pass = 0; pass < QPASS; ++pass) {
+      if (pass > 0) q_load(pass, qx);
+      // (Buffer choices are static, so the compiler can tell these LDS accesses from the DMA
+      // into the K buffers and does not wait for it.)  Chunk i of a thread is in the first
+      // 64 rows iff i < BN * KC / NT.
+      constexpr int QHALF = BN * KC / NT;
+      static_assert(QHALF * NT == BN * KC && 2 * QHALF == QL, "Q chunk split");
+#pragma unroll
+      for (int i = 0; i < QL; ++i) {
+        const int id = tid + NT * i, r = id / KC, c = id % KC;
+        if (i < QHALF) *(u32x4*)(v_lds0 + L::off(r, c)) = qx[i];
+        else *(u32x4*)(v_lds1 + L::off(r - BN, c)) = qx[i];
+      }
+      __builtin_amdgcn_s_waitcnt(waitcnt_imm(63, 0));
+      pipeline_barrier();
+      if (wave / 4 == pass) {  // waves 4 pass .. 4 pass + 3 own these 128 rows
+        if ((wave & 3) < 2) {
+#pragma unroll
+          for (int ks = 0; ks < QKS; ++ks) qreg[ks] = *(const u32x4*)(v_lds0 + op_addr(ks, wave & 1)) ^ p.qflip;
+        } else {
+#pragma unroll
+          for (int ks = 0; ks < QKS; ++ks) qreg[ks] = *(const u32x4*)(v_lds1 + op_addr(ks, wave & 1)) ^ p.qflip;
+        }
+      }
+      __builtin_amdgcn_s_waitcnt(waitcnt_imm(63, 0));
+      pipeline_barrier();
+    }
+  }
   v_dma(0, v_lds0);
   __builtin_amdgcn_s_waitcnt(0x0F70);
   v_store(v_lds0);
   mask_store(m_lds0);
   mask_load(min(1, n_tiles - 1));
-  dma_tile(kg, min(1, n_tiles - 1), k_lds1);
   v_load(min(1, n_tiles - 1));
   __builtin_amdgcn_s_waitcnt(0x0F70);
   mask_store(m_lds1);
