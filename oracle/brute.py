@@ -10,7 +10,8 @@ Definition followed (the FlashAttention forward result; pages: https://yetianai.
 section "传统进化搜索的天花板" for the tiled computation whose result this is, and
 https://yunpan.plus/t/19526-1-1 section "AI生成的代码质量如何？" excerpt 2 for the bitmask
 rule): O[b,i,h] = sum_j softmax_j(scale * <Q[b,i,h], K[b,j,h//G]> over kept j) * V[b,j,h//G],
-and 0 for a row with no kept key.
+and 0 for a row with no kept key; and LSE[b,h,i] = ln sum_{kept j} exp(scale * <Q, K_j>),
+-inf for a row with no kept key.
 """
 
 from __future__ import annotations
@@ -24,15 +25,18 @@ def _d(x: float) -> Decimal:
     return Decimal(float(x))  # exact: every binary float is a finite decimal
 
 
-def attention_brute(q, k, v, mode: str, scale: float, mask=None):
+def attention_brute(q, k, v, mode: str, scale: float, mask=None, with_lse: bool = False):
     """q: nested lists [B][S][Hq][D] of floats; k, v: [B][S][Hkv][D]; mask: [B][Hq][S][W] ints.
 
-    Returns nested lists [B][S][Hq][D] of Decimal."""
+    Returns nested lists [B][S][Hq][D] of Decimal; with_lse=True also returns the
+    log-sum-exp as nested lists [B][Hq][S] of Decimal (Decimal('-Infinity') for a row with
+    no kept key)."""
     B, S, Hq, D = len(q), len(q[0]), len(q[0][0]), len(q[0][0][0])
     Hkv = len(k[0][0])
     G = Hq // Hkv
     sc = _d(scale)
     out = []
+    lse = [[[Decimal("-Infinity")] * S for _ in range(Hq)] for _ in range(B)]
     for b in range(B):
         ob = []
         for i in range(S):
@@ -57,6 +61,7 @@ def attention_brute(q, k, v, mode: str, scale: float, mask=None):
                 m = max(s for _, s in kept)
                 w = [(j, (s - m).exp()) for j, s in kept]
                 den = sum(x for _, x in w)
+                lse[b][h][i] = m + den.ln()
                 row = []
                 for t in range(D):
                     num = sum(x * _d(v[b][j][g][t]) for j, x in w)
@@ -64,4 +69,4 @@ def attention_brute(q, k, v, mode: str, scale: float, mask=None):
                 oi.append(row)
             ob.append(oi)
         out.append(ob)
-    return out
+    return (out, lse) if with_lse else out

@@ -26,6 +26,12 @@ reorder this computation, so the oracle is the definition itself):
         keep   = none: all j;  causal: j <= i;  bitmask: bit (j % 32) of word mask[b,h,i,j//32]
         if no j is kept: O[b,i,h,:] = 0
         else:  w[j] = exp(s[j] - max_kept s) for kept j, 0 otherwise;  O = sum_j w[j] V[b,j,g,:] / sum_j w[j]
+        LSE[b,h,i] = ln sum_{kept j} exp(s[j])  (= max_kept s + ln sum_j w[j]);  -inf if no j is kept
+
+The log-sum-exp is the single-pass softmax state (running max and running sum) that the
+pages' online softmax carries from tile to tile ([avo], "传统进化搜索的天花板": the correction
+step rescales by that state); a forward that also returns it lets a later pass rebuild the
+weights as exp(s[j] - LSE).
 
 Readings where the pages leave a step open (each is listed with its reason in the design notes):
   * a fully masked row outputs exactly 0 (the custom-mask excerpt's finite fill value would
@@ -114,6 +120,18 @@ def masked_softmax(scores: np.ndarray, keep: np.ndarray) -> np.ndarray:
     return np.where(any_kept[:, None], w / np.where(any_kept, den, 1.0)[:, None], 0.0)
 
 
+def masked_logsumexp(scores: np.ndarray, keep: np.ndarray) -> np.ndarray:
+    """Row-wise ln(sum of exp(score)) over kept entries only; -inf for a row with none kept.
+
+    Written as max + ln(sum exp(score - max)) so large scores do not overflow."""
+    any_kept = keep.any(axis=1)
+    m = np.where(keep, scores, -np.inf).max(axis=1)
+    m = np.where(any_kept, m, 0.0)
+    den = np.exp(np.where(keep, scores - m[:, None], -np.inf)).sum(axis=1)
+    with np.errstate(divide="ignore"):
+        return np.where(any_kept, m + np.log(np.where(any_kept, den, 1.0)), -np.inf)
+
+
 def _check(q, k, v, mode, mask):
     if mode not in MODES:
         raise ValueError(f"unknown mode {mode!r}")
@@ -130,12 +148,14 @@ def _check(q, k, v, mode, mask):
 
 
 def attention_rows(q, k, v, mode: str, scale: float, mask=None, rows=None, heads=None,
-                   batches=None, return_weights: bool = False):
+                   batches=None, return_weights: bool = False, return_lse: bool = False):
     """Oracle output for a selection of query rows.
 
     Computes O[b, i, h, :] for b in `batches`, h in `heads`, i in `rows` (all when None),
     as a float64 array [len(batches), len(rows), len(heads), D].  With return_weights=True
-    also returns the attention weights [nb, nrows, nheads, S] (tiny shapes only)."""
+    also returns the attention weights [nb, nrows, nheads, S] (tiny shapes only); with
+    return_lse=True also the log-sum-exp of each row's kept scores [nb, nrows, nheads].
+    Returns O, then the weights, then the LSE, each only when asked for."""
     q, k, v = _f64(q), _f64(k), _f64(v)
     mask = None if mask is None else _u32(mask)
     B, S, Hq, Hkv, D = _check(q, k, v, mode, mask)
@@ -144,6 +164,7 @@ def attention_rows(q, k, v, mode: str, scale: float, mask=None, rows=None, heads
     batches = np.arange(B) if batches is None else np.asarray(batches, dtype=np.int64)
     out = np.zeros((len(batches), len(rows), len(heads), D), dtype=np.float64)
     wts = np.zeros((len(batches), len(rows), len(heads), S)) if return_weights else None
+    lse = np.zeros((len(batches), len(rows), len(heads))) if return_lse else None
     for bi, b in enumerate(batches):
         for hi, h in enumerate(heads):
             g = kv_head_index(int(h), Hq, Hkv)
@@ -157,12 +178,21 @@ def attention_rows(q, k, v, mode: str, scale: float, mask=None, rows=None, heads
                 out[bi, r0:r0 + len(rr), hi, :] = w @ vv
                 if return_weights:
                     wts[bi, r0:r0 + len(rr), hi, :] = w
-    return (out, wts) if return_weights else out
+                if return_lse:
+                    lse[bi, r0:r0 + len(rr), hi] = masked_logsumexp(scores, keep)
+    res = (out,) + ((wts,) if return_weights else ()) + ((lse,) if return_lse else ())
+    return res if len(res) > 1 else out
 
 
 def attention(q, k, v, mode: str, scale: float, mask=None) -> np.ndarray:
     """Full oracle output O [B, S, Hq, D] in float64."""
     return attention_rows(q, k, v, mode, scale, mask)
+
+
+def attention_lse(q, k, v, mode: str, scale: float, mask=None):
+    """Full oracle output and log-sum-exp: O [B, S, Hq, D] and LSE [B, Hq, S], float64."""
+    o, lse = attention_rows(q, k, v, mode, scale, mask, return_lse=True)
+    return o, np.ascontiguousarray(lse.transpose(0, 2, 1))
 
 
 def attention_flops(batch: int, n_q_heads: int, seq_len: int, head_dim: int, mode: str) -> float:

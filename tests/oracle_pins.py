@@ -10,7 +10,10 @@ Each `pin_*` function raises AssertionError when the oracle disagrees with:
     fully masked row == 0, GQA == MHA with K/V repeated per head group, shift of all
     scores by a constant leaves O unchanged even when exp would overflow),
   * a library routine (torch scaled_dot_product_attention in float64 on the CPU, on rows
-    with at least one kept key).
+    with at least one kept key);
+and, for the log-sum-exp of each row, the hand example's values, the brute force, the zero
+scale (log of the kept-key count), one kept key (its scaled dot product), a shift of all
+scores, torch.logsumexp in float64, and exp(score - LSE) == the oracle's weights.
 
 They are plain functions so that tests/test_oracle_mutations.py can plant mistakes in the
 oracle and check that at least one pin fails for each.
@@ -270,6 +273,137 @@ def pin_torch_sdpa_float64():
     got = oracle.attention(q, k, v, "bitmask", scale, mask)
     rows = keep.any(-1).transpose(0, 2, 1)     # [B, S, H]
     np.testing.assert_allclose(got[rows], ref_mask[rows], rtol=1e-11, atol=1e-12)
+
+
+# --------------------------------------------------------------------------- log-sum-exp
+def _lse_value(text):
+    """'ln N' -> ln N, '-inf' -> -inf (the hand example states its values in these forms)."""
+    return -np.inf if text == "-inf" else float(np.log(float(text.split()[1])))
+
+
+def pin_lse_hand_example():
+    g = json.load(open(GOLDEN))
+    q = np.array([[g["q_row"]] * 3])[:, :, None, :]
+    k = np.array([g["k"]])[:, :, None, :]
+    v = np.array([g["v"]])[:, :, None, :]
+    for mode in ("none", "causal", "bitmask"):
+        mask = (np.array(g["mask_words"], dtype=np.uint32).reshape(1, 1, 3, 1)
+                if mode == "bitmask" else None)
+        _, lse = oracle.attention_lse(q, k, v, mode, g["scale"], mask)
+        want = np.array([_lse_value(t) for t in g["expected_lse"][mode]])
+        np.testing.assert_allclose(lse[0, 0], want, rtol=0, atol=1e-14,
+                                   err_msg=f"hand example LSE, mode {mode}")
+
+
+def _brute_lse_compare(seed, B, S, Hq, Hkv, D, mode, scale, density=0.5, empty_rows=()):
+    q, k, v, mask = _rand_case(seed, B, S, Hq, Hkv, D, mode, density)
+    if mask is not None and empty_rows:
+        mask[:, :, list(empty_rows), :] = 0
+    _, want = oracle.attention_brute(q.tolist(), k.tolist(), v.tolist(), mode, scale,
+                                     None if mask is None else mask.tolist(), with_lse=True)
+    want = np.array([[[float(x) for x in row] for row in hh] for hh in want])
+    _, got = oracle.attention_lse(q, k, v, mode, scale, mask)
+    np.testing.assert_array_equal(np.isinf(got), np.isinf(want))
+    fin = np.isfinite(want)
+    np.testing.assert_allclose(got[fin], want[fin], rtol=1e-13, atol=1e-13,
+                               err_msg=f"brute force LSE {mode} S={S}")
+
+
+def pin_lse_brute_force():
+    for i, mode in enumerate(("none", "causal", "bitmask")):
+        _brute_lse_compare(210 + i, 1, 6, 4, 2, 3, mode, 0.7)       # GQA, group 2
+        _brute_lse_compare(220 + i, 2, 5, 2, 2, 4, mode, -1.3)      # negative scale
+        _brute_lse_compare(230 + i, 1, 6, 2, 2, 3, mode, 400.0)     # exp overflows without the max
+    _brute_lse_compare(241, 1, 37, 2, 1, 2, "bitmask", 0.9, density=0.3, empty_rows=(0, 36))
+
+
+def pin_lse_zero_scale_counts_kept_keys():
+    # Every score is 0, so the sum of exp over kept keys is their count.
+    q, k, v, mask = _rand_case(251, B=1, S=40, Hq=2, Hkv=1, D=3, mode="bitmask", density=0.3)
+    mask[0, 1, 5, :] = 0
+    for mode in ("none", "causal", "bitmask"):
+        _, lse = oracle.attention_lse(q, k, v, mode, 0.0, mask)
+        for h in range(2):
+            for i in range(40):
+                if mode == "none":
+                    n = 40
+                elif mode == "causal":
+                    n = i + 1
+                else:
+                    n = sum((int(mask[0, h, i, j // 32]) >> (j % 32)) & 1 for j in range(40))
+                want = np.log(n) if n else -np.inf
+                assert lse[0, h, i] == want or abs(lse[0, h, i] - want) < 1e-14, (mode, h, i)
+
+
+def pin_lse_single_kept_key():
+    # One kept key: the log-sum-exp is that key's scaled dot product, summed by hand here.
+    S, D = 30, 5
+    q, k, v, _ = _rand_case(261, B=1, S=S, Hq=2, Hkv=1, D=D, mode="none")
+    picks = _rng(262).integers(0, S, size=(2, S))
+    keep = np.zeros((1, 2, S, S), dtype=bool)
+    for h in range(2):
+        keep[0, h, np.arange(S), picks[h]] = True
+    _, lse = oracle.attention_lse(q, k, v, "bitmask", -0.45, _pack_bool(keep))
+    for h in range(2):
+        for i in range(S):
+            dot = 0.0
+            for t in range(D):
+                dot += float(q[0, i, h, t]) * float(k[0, picks[h, i], 0, t])
+            assert abs(lse[0, h, i] - (-0.45) * dot) < 1e-12, (h, i)
+
+
+def pin_lse_shift_of_scores():
+    # A coordinate with q = c, k = 1 moves every score of a row by scale*c: the log-sum-exp
+    # moves by exactly that, even when exp of the raw scores would overflow.
+    q, k, v, mask = _rand_case(271, B=1, S=12, Hq=2, Hkv=1, D=3, mode="bitmask")
+    _, base = oracle.attention_lse(q, k, v, "bitmask", 0.5, mask)
+    for c in (5.0, 3000.0):
+        q2 = np.concatenate([q, np.full(q.shape[:-1] + (1,), c)], axis=-1)
+        k2 = np.concatenate([k, np.ones(k.shape[:-1] + (1,))], axis=-1)
+        v2 = np.concatenate([v, np.zeros(v.shape[:-1] + (1,))], axis=-1)
+        _, lse2 = oracle.attention_lse(q2, k2, v2, "bitmask", 0.5, mask)
+        fin = np.isfinite(base)
+        np.testing.assert_allclose(lse2[fin], base[fin] + 0.5 * c, rtol=1e-12, atol=1e-9)
+        assert np.array_equal(np.isinf(lse2), np.isinf(base))
+
+
+def pin_lse_torch_logsumexp():
+    # Library routine: torch.logsumexp in float64 over the scores with masked entries at -inf.
+    q, k, v, mask = _rand_case(281, B=2, S=45, Hq=4, Hkv=2, D=6, mode="bitmask", density=0.4)
+    mask[1, 2, 7, :] = 0
+    scale = 0.8
+    for mode in ("none", "causal", "bitmask"):
+        _, lse = oracle.attention_lse(q, k, v, mode, scale, mask)
+        tq = torch.from_numpy(q).permute(0, 2, 1, 3)                       # [B, Hq, S, D]
+        tk = torch.from_numpy(np.repeat(k, 2, axis=2)).permute(0, 2, 1, 3)
+        sc = scale * (tq @ tk.transpose(-1, -2))
+        i = torch.arange(45)
+        if mode == "causal":
+            sc = sc.masked_fill(i[None, :] > i[:, None], float("-inf"))
+        elif mode == "bitmask":
+            keep = np.zeros((2, 4, 45, 45), dtype=bool)
+            for b in range(2):
+                for h in range(4):
+                    for r in range(45):
+                        keep[b, h, r] = [(int(mask[b, h, r, j // 32]) >> (j % 32)) & 1
+                                         for j in range(45)]
+            sc = sc.masked_fill(~torch.from_numpy(keep), float("-inf"))
+        ref = torch.logsumexp(sc, dim=-1).numpy()
+        np.testing.assert_array_equal(np.isinf(lse), np.isinf(ref))
+        fin = np.isfinite(ref)
+        np.testing.assert_allclose(lse[fin], ref[fin], rtol=1e-12, atol=1e-12)
+
+
+def pin_lse_rebuilds_the_weights():
+    # exp(score - LSE) must be the attention weights the oracle uses for O.
+    q, k, v, mask = _rand_case(291, B=1, S=33, Hq=2, Hkv=1, D=4, mode="bitmask")
+    for mode in ("none", "causal", "bitmask"):
+        _, w, lse = oatt.attention_rows(q, k, v, mode, 0.6, mask, return_weights=True,
+                                        return_lse=True)
+        s = 0.6 * np.einsum("bihd,bjd->bihj", q, k[:, :, 0, :])
+        with np.errstate(invalid="ignore"):
+            rebuilt = np.where(w > 0, np.exp(s - lse[..., None]), 0.0)
+        np.testing.assert_allclose(rebuilt, w, rtol=1e-12, atol=1e-15)
 
 
 ALL_PINS = [f for n, f in sorted(globals().items()) if n.startswith("pin_") and callable(f)]

@@ -75,9 +75,29 @@ def _missing_normalisation(scores, keep):
     return np.where(keep, np.exp(scores - m[:, None]), 0.0)
 
 
+def _lse_log2(scores, keep):
+    return _orig_masked_logsumexp(scores, keep) / np.log(2.0)
+
+
+def _lse_without_max(scores, keep):
+    out = _orig_masked_logsumexp(scores, keep)
+    m = np.where(keep, scores, -np.inf).max(axis=1)
+    return np.where(np.isfinite(out), out - m, out)
+
+
+def _lse_masked_in_sum(scores, keep):
+    return _orig_masked_logsumexp(scores, np.ones_like(keep) & keep.any(axis=1)[:, None])
+
+
+def _lse_empty_row_zero(scores, keep):
+    out = _orig_masked_logsumexp(scores, keep)
+    return np.where(np.isinf(out), 0.0, out)
+
+
 _orig_bit_of = oatt.bit_of
 _orig_keep_rows = oatt.keep_rows
 _orig_masked_softmax = oatt.masked_softmax
+_orig_masked_logsumexp = oatt.masked_logsumexp
 
 MUTATIONS = {
     "gqa_head_modulo": ("kv_head_index", _wrong_kv_head),
@@ -90,6 +110,10 @@ MUTATIONS = {
     "masked_row_mean": ("masked_softmax", _masked_row_mean),
     "softmax_unnormalised": ("masked_softmax", _missing_normalisation),
     "masked_scores_in_max": ("masked_softmax", _masked_not_excluded_from_max),
+    "lse_log2": ("masked_logsumexp", _lse_log2),
+    "lse_without_max": ("masked_logsumexp", _lse_without_max),
+    "lse_masked_in_sum": ("masked_logsumexp", _lse_masked_in_sum),
+    "lse_empty_row_zero": ("masked_logsumexp", _lse_empty_row_zero),
 }
 
 
