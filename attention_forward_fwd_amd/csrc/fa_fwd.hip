@@ -80,6 +80,7 @@ struct Params {
   const u32* mask;
   const uint16_t* vt;  // packed V^T tiles (see VtPack), when the kernel reads V that way
   uint16_t* o;
+  float* lse;  // [B, Hq, S] log-sum-exp of each row's kept scores, or null
   int S, Hq, Hkv, G, W;
   int n_kt;   // 64-key tiles per sequence
   int n_rt;   // row tiles per (batch, kv head)
@@ -828,6 +829,13 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void fa_fwd_kernel(Params
         for (int e = 0; e < 4; ++e) x[e] = oacc[db][4 * t4 + e] * inv;
         *(u32x2*)(orow + 32 * db + 8 * t4 + 4 * hl) = pack4<BF16>(x);
       }
+    // Log-sum-exp of the row's kept scores (natural log), from the running softmax state: the
+    // max m_run is of s*c with c = |scale| log2(e) (Q carries the sign of the scale), and lt
+    // is the sum of 2^(s*c - m_run), so ln(sum exp(scale s)) = (m_run + log2 lt) ln 2.  A row
+    // with no kept key gets -inf.
+    if (p.lse && hl == 0)
+      p.lse[((size_t)b * Hq + my_head) * S + my_pos] =
+          lt > 0.f ? (m_run + __builtin_amdgcn_logf(lt)) * 0.693147180559945f : -INFINITY;
   }
 }
 
@@ -902,7 +910,7 @@ int fa_abi_version(void) { return FA_ABI_VERSION; }
 const char* fa_status_string(int s) {
   switch (s) {
     case FA_OK: return "ok";
-    case FA_ERR_NULL_PTR: return "null q, k, v or o pointer";
+    case FA_ERR_NULL_PTR: return "null q, k, v, o or lse pointer";
     case FA_ERR_BAD_SHAPE: return "bad shape (non-positive size, heads not divisible, or too large)";
     case FA_ERR_UNSUPPORTED: return "unsupported dtype or head_dim, or misaligned pointer";
     case FA_ERR_BAD_MASK_MODE: return "unknown mask mode, or bitmask mode without a mask";
@@ -912,9 +920,15 @@ const char* fa_status_string(int s) {
   }
 }
 
-fa_status fa_fwd(fa_dtype dtype, fa_mask_mode mask_mode, int batch, int n_q_heads,
-                 int n_kv_heads, int seq_len, int head_dim, float scale, const void* q,
-                 const void* k, const void* v, const uint32_t* mask, void* o, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// fa_fwd and fa_fwd_lse: validation first (no HIP call), then the launches.
+fa_status run_fwd(fa_dtype dtype, fa_mask_mode mask_mode, int batch, int n_q_heads,
+                  int n_kv_heads, int seq_len, int head_dim, float scale, const void* q,
+                  const void* k, const void* v, const uint32_t* mask, void* o, float* lse,
+                  void* stream) {
   if (dtype != FA_DTYPE_F16 && dtype != FA_DTYPE_BF16) return FA_ERR_UNSUPPORTED;
   if (mask_mode != FA_MASK_NONE && mask_mode != FA_MASK_CAUSAL && mask_mode != FA_MASK_BITMASK)
     return FA_ERR_BAD_MASK_MODE;
@@ -946,6 +960,7 @@ fa_status fa_fwd(fa_dtype dtype, fa_mask_mode mask_mode, int batch, int n_q_head
   p.v = (const uint16_t*)v;
   p.mask = mask_mode == FA_MASK_BITMASK ? mask : nullptr;
   p.o = (uint16_t*)o;
+  p.lse = lse;
   p.S = seq_len;
   p.Hq = n_q_heads;
   p.Hkv = n_kv_heads;
@@ -995,6 +1010,27 @@ fa_status fa_fwd(fa_dtype dtype, fa_mask_mode mask_mode, int batch, int n_q_head
     if (e == hipSuccess) e = ef;
   }
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+fa_status fa_fwd(fa_dtype dtype, fa_mask_mode mask_mode, int batch, int n_q_heads,
+                 int n_kv_heads, int seq_len, int head_dim, float scale, const void* q,
+                 const void* k, const void* v, const uint32_t* mask, void* o, void* stream) {
+  return run_fwd(dtype, mask_mode, batch, n_q_heads, n_kv_heads, seq_len, head_dim, scale, q, k,
+                 v, mask, o, nullptr, stream);
+}
+
+fa_status fa_fwd_lse(fa_dtype dtype, fa_mask_mode mask_mode, int batch, int n_q_heads,
+                     int n_kv_heads, int seq_len, int head_dim, float scale, const void* q,
+                     const void* k, const void* v, const uint32_t* mask, void* o, float* lse,
+                     void* stream) {
+  if (!lse) return FA_ERR_NULL_PTR;
+  if ((uintptr_t)lse & 3u) return FA_ERR_UNSUPPORTED;
+  return run_fwd(dtype, mask_mode, batch, n_q_heads, n_kv_heads, seq_len, head_dim, scale, q, k,
+                 v, mask, o, lse, stream);
 }
 
 }  // extern "C"

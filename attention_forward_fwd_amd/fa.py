@@ -20,7 +20,7 @@ MODES = {"none": FA_MASK_NONE, "causal": FA_MASK_CAUSAL, "bitmask": FA_MASK_BITM
 DTYPES = {torch.float16: FA_DTYPE_F16, torch.bfloat16: FA_DTYPE_BF16}
 STATUS = {0: "FA_OK", 1: "FA_ERR_NULL_PTR", 2: "FA_ERR_BAD_SHAPE", 3: "FA_ERR_UNSUPPORTED",
           4: "FA_ERR_BAD_MASK_MODE", 5: "FA_ERR_BAD_SCALE", 6: "FA_ERR_HIP"}
-EXPORTS = ("fa_fwd", "fa_status_string", "fa_abi_version")
+EXPORTS = ("fa_fwd", "fa_fwd_lse", "fa_status_string", "fa_abi_version")
 
 _lib = None
 
@@ -47,6 +47,8 @@ def load() -> ctypes.CDLL:
                                ctypes.c_int, ctypes.c_int, ctypes.c_float, ctypes.c_void_p,
                                ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                ctypes.c_void_p]
+        lib.fa_fwd_lse.restype = ctypes.c_int
+        lib.fa_fwd_lse.argtypes = lib.fa_fwd.argtypes[:13] + [ctypes.c_void_p, ctypes.c_void_p]
         lib.fa_status_string.restype = ctypes.c_char_p
         lib.fa_status_string.argtypes = [ctypes.c_int]
         lib.fa_abi_version.restype = ctypes.c_int
@@ -67,13 +69,16 @@ def fa_fwd_raw(dtype: int, mask_mode: int, batch: int, n_q_heads: int, n_kv_head
                          ctypes.c_float(scale), q, k, v, mask, o, stream)
 
 
-def fa_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, mode: str = "none",
-           scale: float | None = None, mask: torch.Tensor | None = None,
-           out: torch.Tensor | None = None) -> torch.Tensor:
-    """O = softmax(scale Q K^T + mask) V on the GPU (see include/fa.h for the definition).
+def fa_fwd_lse_raw(dtype: int, mask_mode: int, batch: int, n_q_heads: int, n_kv_heads: int,
+                   seq_len: int, head_dim: int, scale: float, q: int, k: int, v: int, mask: int,
+                   o: int, lse: int, stream: int) -> int:
+    """Direct call of fa_fwd_lse with integer pointers; returns the fa_status code."""
+    return load().fa_fwd_lse(dtype, mask_mode, batch, n_q_heads, n_kv_heads, seq_len, head_dim,
+                             ctypes.c_float(scale), q, k, v, mask, o, lse, stream)
 
-    q [B,S,Hq,D], k/v [B,S,Hkv,D] (bf16 or fp16, contiguous, on one GPU); mask [B,Hq,S,ceil(S/32)]
-    int32/uint32 words for mode "bitmask".  Enqueued on torch's current stream; returns o."""
+
+def _args(q, k, v, mode, scale, mask, out):
+    """Checks the tensors and returns (B, S, Hq, Hkv, D, scale, mask pointer, out)."""
     if mode not in MODES:
         raise ValueError(f"mode must be one of {sorted(MODES)}")
     for name, t in (("q", q), ("k", k), ("v", v)):
@@ -105,10 +110,43 @@ def fa_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, mode: str = "none"
         out = torch.empty_like(q)
     elif out.shape != q.shape or out.dtype != q.dtype or not out.is_contiguous():
         raise ValueError("out must be a contiguous tensor like q")
+    return B, S, Hq, Hkv, D, float(scale), mptr, out
+
+
+def fa_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, mode: str = "none",
+           scale: float | None = None, mask: torch.Tensor | None = None,
+           out: torch.Tensor | None = None) -> torch.Tensor:
+    """O = softmax(scale Q K^T + mask) V on the GPU (see include/fa.h for the definition).
+
+    q [B,S,Hq,D], k/v [B,S,Hkv,D] (bf16 or fp16, contiguous, on one GPU); mask [B,Hq,S,ceil(S/32)]
+    int32/uint32 words for mode "bitmask".  Enqueued on torch's current stream; returns o."""
+    B, S, Hq, Hkv, D, scale, mptr, out = _args(q, k, v, mode, scale, mask, out)
     stream = torch.cuda.current_stream(q.device).cuda_stream
     with torch.cuda.device(q.device):
-        st = fa_fwd_raw(DTYPES[q.dtype], MODES[mode], B, Hq, Hkv, S, D, float(scale),
-                        q.data_ptr(), k.data_ptr(), v.data_ptr(), mptr, out.data_ptr(), stream)
+        st = fa_fwd_raw(DTYPES[q.dtype], MODES[mode], B, Hq, Hkv, S, D, scale, q.data_ptr(),
+                        k.data_ptr(), v.data_ptr(), mptr, out.data_ptr(), stream)
     if st != 0:
         raise FaError(st, fa_status_string(st))
     return out
+
+
+def fa_fwd_lse(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, mode: str = "none",
+               scale: float | None = None, mask: torch.Tensor | None = None,
+               out: torch.Tensor | None = None, lse: torch.Tensor | None = None):
+    """As fa_fwd, also returning the log-sum-exp of each row's kept scores.
+
+    Returns (o, lse) with lse [B, Hq, S] float32 (-inf for a row with no kept key)."""
+    B, S, Hq, Hkv, D, scale, mptr, out = _args(q, k, v, mode, scale, mask, out)
+    if lse is None:
+        lse = torch.empty((B, Hq, S), dtype=torch.float32, device=q.device)
+    elif (tuple(lse.shape) != (B, Hq, S) or lse.dtype != torch.float32 or not lse.is_contiguous()
+          or lse.device != q.device):
+        raise ValueError(f"lse must be a contiguous float32 tensor of shape {(B, Hq, S)} on q's device")
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    with torch.cuda.device(q.device):
+        st = fa_fwd_lse_raw(DTYPES[q.dtype], MODES[mode], B, Hq, Hkv, S, D, scale, q.data_ptr(),
+                            k.data_ptr(), v.data_ptr(), mptr, out.data_ptr(), lse.data_ptr(),
+                            stream)
+    if st != 0:
+        raise FaError(st, fa_status_string(st))
+    return out, lse

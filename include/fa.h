@@ -58,7 +58,7 @@
 extern "C" {
 #endif
 
-#define FA_ABI_VERSION 1
+#define FA_ABI_VERSION 2
 
 typedef enum {
   FA_MASK_NONE = 0,     /* every key kept */
@@ -70,7 +70,7 @@ typedef enum { FA_DTYPE_F16 = 0, FA_DTYPE_BF16 = 1 } fa_dtype;
 
 typedef enum {
   FA_OK = 0,
-  FA_ERR_NULL_PTR = 1,      /* q, k, v or o is NULL */
+  FA_ERR_NULL_PTR = 1,      /* q, k, v or o (or fa_fwd_lse's lse) is NULL */
   FA_ERR_BAD_SHAPE = 2,     /* batch, seq_len or a head count <= 0, n_q_heads % n_kv_heads != 0,
                                or a tensor larger than 2^31 elements per batch */
   FA_ERR_UNSUPPORTED = 3,   /* head_dim not 64 or 128, unknown dtype, misaligned pointer */
@@ -83,6 +83,25 @@ typedef enum {
 fa_status fa_fwd(fa_dtype dtype, fa_mask_mode mask_mode, int batch, int n_q_heads,
                  int n_kv_heads, int seq_len, int head_dim, float scale, const void* q,
                  const void* k, const void* v, const uint32_t* mask, void* o, void* stream);
+
+/* Forward attention as fa_fwd, plus the log-sum-exp of each row's kept scaled scores:
+ *     lse[b, h, i] = ln sum_{kept j} exp(s_j)      (s_j and "kept" as defined above),
+ *     lse[b, h, i] = -inf when row i keeps no key.
+ * This is the running softmax state (running max and running sum) that the online softmax
+ * carries from tile to tile -- https://yetianai.com/news/16520, section "传统进化搜索的天花板"
+ * (FA4's correction step rescales by it) -- returned so that a later pass can rebuild the
+ * weights as exp(s_j - lse) without recomputing the row sums.
+ *   lse  [batch, n_q_heads, seq_len] float32, DEVICE pointer owned by the caller, 4-byte
+ *        aligned, not overlapping q, k, v, mask or o.  Every element is written.
+ * Numerics: computed in fp32 from the same rounded weights that normalise O, so its error
+ * against the exact value is at most about the relative rounding step of the input dtype
+ * (2^-8 for bf16, 2^-11 for fp16).  o, the work enqueued, memory use and errors are as for
+ * fa_fwd (o is bitwise the same); lse == NULL is FA_ERR_NULL_PTR, a misaligned lse
+ * FA_ERR_UNSUPPORTED. */
+fa_status fa_fwd_lse(fa_dtype dtype, fa_mask_mode mask_mode, int batch, int n_q_heads,
+                     int n_kv_heads, int seq_len, int head_dim, float scale, const void* q,
+                     const void* k, const void* v, const uint32_t* mask, void* o, float* lse,
+                     void* stream);
 
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char* fa_status_string(int status);

@@ -53,7 +53,9 @@ def test_no_vendor_math_library_linked():
 
 def test_abi_version_and_status_strings():
     lib = _lib()
-    assert lib.fa_abi_version() == 1
+    assert lib.fa_abi_version() == 2
+    header = open(HEADER).read()
+    assert re.search(r"#define FA_ABI_VERSION 2\b", header)
     for code, name in fab.STATUS.items():
         s = fa.fa_status_string(code)
         assert s and isinstance(s, str)
@@ -86,12 +88,33 @@ def test_invalid_arguments_rejected_before_launch(kw, status):
     assert _call(**kw) == status
 
 
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=0), 1), (dict(o=0), 1), (dict(D=96), 3), (dict(mode=2, mask=0), 4),
+    (dict(scale=float("nan")), 5), (dict(S=0), 2),
+])
+def test_lse_entry_invalid_arguments_rejected(kw, status):
+    # fa_fwd_lse validates like fa_fwd, given a valid lse pointer
+    _lib()
+    a = dict(dtype=1, mode=0, B=1, Hq=2, Hkv=1, S=8, D=128, scale=0.1, q=P, k=P, v=P, mask=0, o=P)
+    a.update(kw)
+    assert fa.fa_fwd_lse_raw(a["dtype"], a["mode"], a["B"], a["Hq"], a["Hkv"], a["S"], a["D"],
+                             a["scale"], a["q"], a["k"], a["v"], a["mask"], a["o"], P, 0) == status
+
+
+@pytest.mark.parametrize("lse,status", [(0, 1), (P + 2, 3)])
+def test_lse_pointer_checked(lse, status):
+    _lib()
+    assert fa.fa_fwd_lse_raw(1, 0, 1, 2, 1, 8, 128, 0.1, P, P, P, 0, P, lse, 0) == status
+
+
 def test_python_binding_refuses_cpu_tensors():
     import torch
     _lib()
     q = torch.zeros(1, 8, 2, 64, dtype=torch.bfloat16)
     with pytest.raises(ValueError, match="GPU"):
         fa.fa_fwd(q, q, q)
+    with pytest.raises(ValueError, match="GPU"):
+        fa.fa_fwd_lse(q, q, q)
 
 
 def test_kernel_launch_stubs_defined():
