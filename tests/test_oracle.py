@@ -1,11 +1,12 @@
-"""CPU checks of the fp64 oracle against facts fixed outside it (see oracle_pins.py)."""
+"""CPU checks of the oracle against facts fixed outside it (see oracle_pins.py, mask_pins.py)."""
 
 import pytest
 
+import mask_pins
 import oracle_pins
 
 
-@pytest.mark.parametrize("pin", oracle_pins.ALL_PINS, ids=lambda f: f.__name__)
+@pytest.mark.parametrize("pin", oracle_pins.ALL_PINS + mask_pins.ALL_PINS, ids=lambda f: f.__name__)
 def test_oracle_pin(pin):
     pin()
 

@@ -7,7 +7,9 @@ one test) with a subtly wrong version; at least one pin in oracle_pins.py must t
 import numpy as np
 import pytest
 
+import mask_pins
 import oracle_pins
+from oracle import mask_pack as opack
 from oracle import masked_attention as oatt
 
 
@@ -126,6 +128,63 @@ def _any_pin_fails():
         except AssertionError:
             failed.append(pin.__name__)
     return failed
+
+
+def _keep_only_ones(mask_bytes):
+    # only the byte value 1 keeps (other nonzero values dropped)
+    if hasattr(mask_bytes, "detach"):
+        mask_bytes = mask_bytes.detach().cpu().numpy()
+    return np.asarray(mask_bytes) == 1
+
+
+def _summary_32_rows(mask_bytes):
+    # row blocks of 32 instead of 64 (the first half of every block only)
+    keep = _orig_keep_of(mask_bytes).copy()
+    S = keep.shape[-1]
+    for r0 in range(32, S, 64):
+        keep[:, :, r0:r0 + 32, :] = False
+    return _orig_tile_summary(keep.astype(np.uint8))
+
+
+def _summary_transposed(mask_bytes):
+    keep = _orig_keep_of(mask_bytes)
+    return _orig_tile_summary(np.swapaxes(keep, -1, -2).astype(np.uint8))
+
+
+def _pack_msb_first(mask_bytes):
+    w = _orig_pack_mask(mask_bytes)
+    out = np.zeros_like(w)
+    for k in range(32):
+        out |= ((w >> np.uint32(k)) & np.uint32(1)) << np.uint32(31 - k)
+    return out
+
+
+_orig_keep_of = opack.keep_of
+_orig_tile_summary = opack.tile_summary
+_orig_pack_mask = opack.pack_mask
+
+PACK_MUTATIONS = {
+    "pack_only_byte_one": ("keep_of", _keep_only_ones),
+    "pack_msb_first": ("pack_mask", _pack_msb_first),
+    "summary_32_rows": ("tile_summary", _summary_32_rows),
+    "summary_transposed": ("tile_summary", _summary_transposed),
+}
+
+
+@pytest.mark.parametrize("name", sorted(PACK_MUTATIONS))
+def test_pack_mutation_is_caught(name, monkeypatch):
+    import oracle
+    attr, fn = PACK_MUTATIONS[name]
+    monkeypatch.setattr(opack, attr, fn)
+    if hasattr(oracle, attr):
+        monkeypatch.setattr(oracle, attr, fn)
+    failed = []
+    for pin in mask_pins.ALL_PINS:
+        try:
+            pin()
+        except AssertionError:
+            failed.append(pin.__name__)
+    assert failed, f"planted mistake {name!r} in oracle.mask_pack.{attr} passed every pin"
 
 
 @pytest.mark.parametrize("name", sorted(MUTATIONS))
