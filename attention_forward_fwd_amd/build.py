@@ -10,7 +10,7 @@ import sys
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 INCLUDE = os.path.join(ROOT, "include")
-SOURCES = [os.path.join(PKG, "csrc", "fa_fwd.hip")]
+SOURCES = [os.path.join(PKG, "csrc", "fa_fwd.hip"), os.path.join(PKG, "csrc", "fa_mask.hip")]
 LIB = os.path.join(PKG, "libfa.so")
 
 # -packed-fp32-ops: keep the compiler from emitting packed fp32 VALU instructions.

@@ -20,7 +20,8 @@ MODES = {"none": FA_MASK_NONE, "causal": FA_MASK_CAUSAL, "bitmask": FA_MASK_BITM
 DTYPES = {torch.float16: FA_DTYPE_F16, torch.bfloat16: FA_DTYPE_BF16}
 STATUS = {0: "FA_OK", 1: "FA_ERR_NULL_PTR", 2: "FA_ERR_BAD_SHAPE", 3: "FA_ERR_UNSUPPORTED",
           4: "FA_ERR_BAD_MASK_MODE", 5: "FA_ERR_BAD_SCALE", 6: "FA_ERR_HIP"}
-EXPORTS = ("fa_fwd", "fa_fwd_lse", "fa_status_string", "fa_abi_version")
+EXPORTS = ("fa_fwd", "fa_fwd_lse", "fa_pack_mask", "fa_mask_tiles", "fa_status_string",
+           "fa_abi_version")
 
 _lib = None
 
@@ -49,6 +50,11 @@ def load() -> ctypes.CDLL:
                                ctypes.c_void_p]
         lib.fa_fwd_lse.restype = ctypes.c_int
         lib.fa_fwd_lse.argtypes = lib.fa_fwd.argtypes[:13] + [ctypes.c_void_p, ctypes.c_void_p]
+        for name in ("fa_pack_mask", "fa_mask_tiles"):
+            f = getattr(lib, name)
+            f.restype = ctypes.c_int
+            f.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                          ctypes.c_void_p, ctypes.c_void_p]
         lib.fa_status_string.restype = ctypes.c_char_p
         lib.fa_status_string.argtypes = [ctypes.c_int]
         lib.fa_abi_version.restype = ctypes.c_int
@@ -150,3 +156,60 @@ def fa_fwd_lse(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, mode: str = "n
     if st != 0:
         raise FaError(st, fa_status_string(st))
     return out, lse
+
+
+def fa_pack_mask_raw(batch: int, n_heads: int, seq_len: int, mask_bytes: int, mask_words: int,
+                     stream: int) -> int:
+    return load().fa_pack_mask(batch, n_heads, seq_len, mask_bytes, mask_words, stream)
+
+
+def fa_mask_tiles_raw(batch: int, n_heads: int, seq_len: int, mask_words: int, tiles: int,
+                      stream: int) -> int:
+    return load().fa_mask_tiles(batch, n_heads, seq_len, mask_words, tiles, stream)
+
+
+def pack_mask(mask: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
+    """Byte or bool mask [B, H, S, S] on the GPU (nonzero keeps) -> int32 words [B, H, S, ceil(S/32)]
+    in the layout fa_fwd reads (see include/fa.h)."""
+    if not mask.is_cuda or not mask.is_contiguous():
+        raise ValueError("mask must be a contiguous GPU tensor (there is no CPU path)")
+    if mask.dtype not in (torch.uint8, torch.bool, torch.int8) or mask.dim() != 4:
+        raise ValueError("mask must be a 4-D uint8/int8/bool tensor [B, H, S, S]")
+    B, H, S, S2 = mask.shape
+    if S != S2:
+        raise ValueError("mask must be square in its last two dimensions")
+    W = (S + 31) // 32
+    if out is None:
+        out = torch.empty((B, H, S, W), dtype=torch.int32, device=mask.device)
+    elif tuple(out.shape) != (B, H, S, W) or out.dtype != torch.int32 or not out.is_contiguous():
+        raise ValueError(f"out must be a contiguous int32 tensor of shape {(B, H, S, W)}")
+    stream = torch.cuda.current_stream(mask.device).cuda_stream
+    with torch.cuda.device(mask.device):
+        st = fa_pack_mask_raw(B, H, S, mask.data_ptr(), out.data_ptr(), stream)
+    if st != 0:
+        raise FaError(st, fa_status_string(st))
+    return out
+
+
+def mask_tiles(words: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
+    """Packed mask words [B, H, S, ceil(S/32)] on the GPU -> int32 summary [B, H, R, ceil(R/32)],
+    R = ceil(S/64): bit t of block r set iff rows [64r, 64r+64) x keys [64t, 64t+64) keep a key."""
+    if not words.is_cuda or not words.is_contiguous() or words.dim() != 4:
+        raise ValueError("words must be a contiguous 4-D GPU tensor")
+    if words.dtype not in (torch.int32, getattr(torch, "uint32", torch.int32)):
+        raise ValueError("words must hold 32-bit words")
+    B, H, S, W = words.shape
+    if W != (S + 31) // 32:
+        raise ValueError("words must be [B, H, S, ceil(S/32)]")
+    R = (S + 63) // 64
+    TW = (R + 31) // 32
+    if out is None:
+        out = torch.empty((B, H, R, TW), dtype=torch.int32, device=words.device)
+    elif tuple(out.shape) != (B, H, R, TW) or out.dtype != torch.int32 or not out.is_contiguous():
+        raise ValueError(f"out must be a contiguous int32 tensor of shape {(B, H, R, TW)}")
+    stream = torch.cuda.current_stream(words.device).cuda_stream
+    with torch.cuda.device(words.device):
+        st = fa_mask_tiles_raw(B, H, S, words.data_ptr(), out.data_ptr(), stream)
+    if st != 0:
+        raise FaError(st, fa_status_string(st))
+    return out

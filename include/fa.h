@@ -58,7 +58,7 @@
 extern "C" {
 #endif
 
-#define FA_ABI_VERSION 2
+#define FA_ABI_VERSION 3
 
 typedef enum {
   FA_MASK_NONE = 0,     /* every key kept */
@@ -102,6 +102,33 @@ fa_status fa_fwd_lse(fa_dtype dtype, fa_mask_mode mask_mode, int batch, int n_q_
                      int n_kv_heads, int seq_len, int head_dim, float scale, const void* q,
                      const void* k, const void* v, const uint32_t* mask, void* o, float* lse,
                      void* stream);
+
+/* Packs a byte mask into the layout fa_fwd reads in FA_MASK_BITMASK mode.
+ *   mask_bytes [batch, n_heads, seq_len, seq_len] uint8, one byte per (query row, key):
+ *              nonzero keeps the score.  Any alignment (16-byte aligned rows load faster).
+ *   mask_words [batch, n_heads, seq_len, W] uint32, W = ceil(seq_len / 32), 4-byte aligned:
+ *              bit j % 32 of word j / 32 of a row = (byte j != 0), least significant bit
+ *              first; the padding bits of the last word (keys >= seq_len) are written as 0.
+ * Layout from https://yunpan.plus/t/19526-1-1, section "AI生成的代码质量如何？", excerpt 2.
+ * Both are DEVICE pointers owned by the caller and must not overlap.  One kernel is enqueued
+ * on `stream`; nothing is allocated.  Errors: NULL pointer -> FA_ERR_NULL_PTR; a size <= 0
+ * or a grid past 2^31 blocks -> FA_ERR_BAD_SHAPE; misaligned mask_words ->
+ * FA_ERR_UNSUPPORTED; launch failure -> FA_ERR_HIP. */
+fa_status fa_pack_mask(int batch, int n_heads, int seq_len, const uint8_t* mask_bytes,
+                       uint32_t* mask_words, void* stream);
+
+/* Per-tile summary of a packed mask: which 64 x 64 blocks of (query rows, keys) hold a kept
+ * bit -- the tile a kernel may skip outright (same page, excerpt 1: a tile with no set mask
+ * bit does no matrix work).
+ *   mask_words [batch, n_heads, seq_len, W] uint32 as above (padding bits are ignored).
+ *   tiles      [batch, n_heads, R, TW] uint32 with R = ceil(seq_len / 64) row blocks and
+ *              TW = ceil(R / 32) words per block: bit t % 32 of word t / 32 of block r is set
+ *              iff some kept bit lies in rows [64 r, 64 r + 64) x keys [64 t, 64 t + 64)
+ *              (clipped to seq_len); bits for t >= R are 0.
+ * DEVICE pointers owned by the caller, 4-byte aligned, not overlapping.  One kernel on
+ * `stream`; nothing allocated.  Errors as for fa_pack_mask. */
+fa_status fa_mask_tiles(int batch, int n_heads, int seq_len, const uint32_t* mask_words,
+                        uint32_t* tiles, void* stream);
 
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char* fa_status_string(int status);

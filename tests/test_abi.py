@@ -53,9 +53,9 @@ def test_no_vendor_math_library_linked():
 
 def test_abi_version_and_status_strings():
     lib = _lib()
-    assert lib.fa_abi_version() == 2
+    assert lib.fa_abi_version() == 3
     header = open(HEADER).read()
-    assert re.search(r"#define FA_ABI_VERSION 2\b", header)
+    assert re.search(r"#define FA_ABI_VERSION 3\b", header)
     for code, name in fab.STATUS.items():
         s = fa.fa_status_string(code)
         assert s and isinstance(s, str)
@@ -107,6 +107,17 @@ def test_lse_pointer_checked(lse, status):
     assert fa.fa_fwd_lse_raw(1, 0, 1, 2, 1, 8, 128, 0.1, P, P, P, 0, P, lse, 0) == status
 
 
+@pytest.mark.parametrize("fn", ["fa_pack_mask_raw", "fa_mask_tiles_raw"])
+@pytest.mark.parametrize("args,status", [
+    ((1, 1, 8, 0, P, 0), 1), ((1, 1, 8, P, 0, 0), 1), ((0, 1, 8, P, P, 0), 2),
+    ((1, 0, 8, P, P, 0), 2), ((1, 1, 0, P, P, 0), 2), ((1, 1, -3, P, P, 0), 2),
+    ((1, 1, 8, P, P + 2, 0), 3), ((1 << 20, 64, 1 << 14, P, P, 0), 2),
+])
+def test_mask_entries_validate(fn, args, status):
+    _lib()
+    assert getattr(fa, fn)(*args) == status
+
+
 def test_python_binding_refuses_cpu_tensors():
     import torch
     _lib()
@@ -115,6 +126,10 @@ def test_python_binding_refuses_cpu_tensors():
         fa.fa_fwd(q, q, q)
     with pytest.raises(ValueError, match="GPU"):
         fa.fa_fwd_lse(q, q, q)
+    with pytest.raises(ValueError, match="GPU"):
+        fa.pack_mask(torch.zeros(1, 1, 8, 8, dtype=torch.uint8))
+    with pytest.raises(ValueError, match="GPU"):
+        fa.mask_tiles(torch.zeros(1, 1, 8, 1, dtype=torch.int32))
 
 
 def test_kernel_launch_stubs_defined():
