@@ -81,6 +81,9 @@ struct Params {
   const uint16_t* vt;  // packed V^T tiles (see VtPack), when the kernel reads V that way
   uint16_t* o;
   float* lse;  // [B, Hq, S] log-sum-exp of each row's kept scores, or null
+  const u32* tiles;  // bitmask mode: [B, Hq, n_rb, TW] summary of 64x64 blocks with a kept bit,
+                     // or null (then every key tile is visited)
+  int n_rb, TW;      // 64-row blocks per head, summary words per block
   int S, Hq, Hkv, G, W;
   int n_kt;   // 64-key tiles per sequence
   int n_rt;   // row tiles per (batch, kv head)
@@ -100,6 +103,7 @@ constexpr int kWide = 8;          // waves of the 256-row workgroup
 constexpr int kWideRows = 8192;   // rows per KV head (S x G) from which it is used
 constexpr int kWideRowsCausal = 16384;  // (causal: its longer tail pays off later)
 constexpr int kPackRowTiles = 8;  // row tiles per KV head from which V is packed once up front
+constexpr int kMaxListTiles = 2048;  // key tiles a workgroup can list from a tile summary
 #ifndef FA_P1_VALU
 #define FA_P1_VALU 8
 #endif
@@ -428,6 +432,64 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void fa_fwd_kernel(Params
     n_tiles = (S + BN - 1) / BN;
   }
 
+  // Bitmask mode with a tile summary: the workgroup visits only the key tiles in which some row
+  // of its positions and heads keeps a key (the OR of the summary words of its G heads and the
+  // 64-row blocks its positions touch; a superset of the live tiles, so nothing kept is
+  // dropped), listed in LDS in increasing order.  Waves still skip the listed tiles they have
+  // no kept bit in by the ballot.  Tile j of the walk is tix(j).
+  __shared__ uint16_t tlist[MODE == kBitmask ? kMaxListTiles : 1];
+  __shared__ int tcount;
+  bool sparse = false;
+  if constexpr (MODE == kBitmask) {
+    if (p.tiles) {
+      sparse = true;
+      if (wave == 0) {
+        const int rb0 = (row0 / G) / 64, rb1 = min((row0 + BM - 1) / G, S - 1) / 64;
+        u32 word = 0u;
+        if (lane < p.TW) {  // TW <= 64 words of 32 tiles
+          for (int g = 0; g < G; ++g)
+            for (int rb = rb0; rb <= rb1; ++rb)
+              word |= p.tiles[(((size_t)b * Hq + hk * G + g) * p.n_rb + rb) * p.TW + lane];
+        }
+        // exclusive prefix sum of the popcounts over the 64 lanes, then each lane lists its bits
+        const int pc = __popc(word);
+        int incl = pc;
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+          const int y = __shfl_up(incl, d);
+          if (lane >= d) incl += y;
+        }
+        int pos = incl - pc;
+        while (word) {
+          const int bit = __ffs((int)word) - 1;
+          tlist[pos++] = (uint16_t)(lane * 32 + bit);
+          word &= word - 1u;
+        }
+        if (lane == 63) tcount = incl;
+      }
+      __syncthreads();
+      n_tiles = __builtin_amdgcn_readfirstlane(tcount);
+    }
+  }
+  auto tix = [&](int j) __attribute__((always_inline)) {
+    const int jj = min(j, n_tiles - 1);
+    if constexpr (MODE == kBitmask) {
+      if (sparse) return __builtin_amdgcn_readfirstlane((int)tlist[jj]);
+    }
+    return jj;
+  };
+  if (n_tiles == 0) {  // (tile summary) no key of these rows is kept: O = 0, LSE = -inf
+    if (wave_live && my_pos < S) {
+      uint16_t* orow = p.o + q_batch + ((size_t)my_pos * Hq + my_head) * D;
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int t4 = 0; t4 < 4; ++t4) *(u32x2*)(orow + 32 * db + 8 * t4 + 4 * hl) = (u32x2){0u, 0u};
+      if (p.lse && hl == 0) p.lse[((size_t)b * Hq + my_head) * S + my_pos] = -INFINITY;
+    }
+    return;
+  }
+
   // Lane bases of the 128-bit operand reads (Q and K): row l32 of a 32-row block, chunk
   // 2ks + hl.  At d=64 the row XOR depends on ks & 1, hence two bases.
   int op_base[2];
@@ -715,7 +777,7 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void fa_fwd_kernel(Params
                   f32x16 (&s_nxt)[NKB], const unsigned char* k_nxt, unsigned char* k_fill,
                   const unsigned char* v_cur, unsigned char* v_fill, const u32* m_nxt,
                   u32* m_fill) __attribute__((always_inline)) {
-    const int j1 = min(j + 1, n_tiles - 1), j2 = min(j + 2, n_tiles - 1);
+    const int j1 = tix(j + 1), j2 = tix(j + 2);
     auto issue_loads = [&]() __attribute__((always_inline)) {
       mask_load(j2);
       dma_tile(kg, j2, k_fill);
@@ -762,10 +824,10 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void fa_fwd_kernel(Params
   {
     u32x4 qx[QL];
     q_load(0, qx);
-    dma_tile(kg, 0, k_lds0);
-    dma_tile(kg, min(1, n_tiles - 1), k_lds1);
-    v_load(0);
-    mask_load(0);
+    dma_tile(kg, tix(0), k_lds0);
+    dma_tile(kg, tix(1), k_lds1);
+    v_load(tix(0));
+    mask_load(tix(0));
 #pragma unroll
     for (int pass = 0; pass < QPASS; ++pass) {
       if (pass > 0) q_load(pass, qx);
@@ -795,16 +857,16 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void fa_fwd_kernel(Params
       pipeline_barrier();
     }
   }
-  v_dma(0, v_lds0);
+  v_dma(tix(0), v_lds0);
   __builtin_amdgcn_s_waitcnt(0x0F70);
   v_store(v_lds0);
   mask_store(m_lds0);
-  mask_load(min(1, n_tiles - 1));
-  v_load(min(1, n_tiles - 1));
+  mask_load(tix(1));
+  v_load(tix(1));
   __builtin_amdgcn_s_waitcnt(0x0F70);
   mask_store(m_lds1);
   __syncthreads();
-  cls_cur = classify(0, m_lds0);
+  cls_cur = classify(tix(0), m_lds0);
   live_cur = wave_live && !cls_cur.skip;
   retire(cls_cur, live_cur);
   if (live_cur) qk(k_lds0, sA);
@@ -924,11 +986,11 @@ const char* fa_status_string(int s) {
 
 namespace {
 
-// fa_fwd and fa_fwd_lse: validation first (no HIP call), then the launches.
+// fa_fwd, fa_fwd_lse and fa_fwd_ex: validation first (no HIP call), then the launches.
 fa_status run_fwd(fa_dtype dtype, fa_mask_mode mask_mode, int batch, int n_q_heads,
                   int n_kv_heads, int seq_len, int head_dim, float scale, const void* q,
-                  const void* k, const void* v, const uint32_t* mask, void* o, float* lse,
-                  void* stream) {
+                  const void* k, const void* v, const uint32_t* mask, const uint32_t* tiles,
+                  void* o, float* lse, void* stream) {
   if (dtype != FA_DTYPE_F16 && dtype != FA_DTYPE_BF16) return FA_ERR_UNSUPPORTED;
   if (mask_mode != FA_MASK_NONE && mask_mode != FA_MASK_CAUSAL && mask_mode != FA_MASK_BITMASK)
     return FA_ERR_BAD_MASK_MODE;
@@ -953,6 +1015,12 @@ fa_status run_fwd(fa_dtype dtype, fa_mask_mode mask_mode, int batch, int n_q_hea
   if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o) & 15u) return FA_ERR_UNSUPPORTED;
   if (mask_mode == FA_MASK_BITMASK && (!mask || ((uintptr_t)mask & 3u))) return FA_ERR_BAD_MASK_MODE;
   if (!isfinite(scale)) return FA_ERR_BAD_SCALE;
+  if (lse && ((uintptr_t)lse & 3u)) return FA_ERR_UNSUPPORTED;
+  const int n_rb = (seq_len + 63) / 64;
+  if (tiles) {
+    if (mask_mode != FA_MASK_BITMASK) return FA_ERR_BAD_MASK_MODE;
+    if (((uintptr_t)tiles & 3u) || n_rb > kMaxListTiles) return FA_ERR_UNSUPPORTED;
+  }
 
   Params p;
   p.q = (const uint16_t*)q;
@@ -961,6 +1029,9 @@ fa_status run_fwd(fa_dtype dtype, fa_mask_mode mask_mode, int batch, int n_q_hea
   p.mask = mask_mode == FA_MASK_BITMASK ? mask : nullptr;
   p.o = (uint16_t*)o;
   p.lse = lse;
+  p.tiles = tiles;
+  p.n_rb = n_rb;
+  p.TW = (n_rb + 31) / 32;
   p.S = seq_len;
   p.Hq = n_q_heads;
   p.Hkv = n_kv_heads;
@@ -1020,7 +1091,7 @@ fa_status fa_fwd(fa_dtype dtype, fa_mask_mode mask_mode, int batch, int n_q_head
                  int n_kv_heads, int seq_len, int head_dim, float scale, const void* q,
                  const void* k, const void* v, const uint32_t* mask, void* o, void* stream) {
   return run_fwd(dtype, mask_mode, batch, n_q_heads, n_kv_heads, seq_len, head_dim, scale, q, k,
-                 v, mask, o, nullptr, stream);
+                 v, mask, nullptr, o, nullptr, stream);
 }
 
 fa_status fa_fwd_lse(fa_dtype dtype, fa_mask_mode mask_mode, int batch, int n_q_heads,
@@ -1028,9 +1099,16 @@ fa_status fa_fwd_lse(fa_dtype dtype, fa_mask_mode mask_mode, int batch, int n_q_
                      const void* k, const void* v, const uint32_t* mask, void* o, float* lse,
                      void* stream) {
   if (!lse) return FA_ERR_NULL_PTR;
-  if ((uintptr_t)lse & 3u) return FA_ERR_UNSUPPORTED;
   return run_fwd(dtype, mask_mode, batch, n_q_heads, n_kv_heads, seq_len, head_dim, scale, q, k,
-                 v, mask, o, lse, stream);
+                 v, mask, nullptr, o, lse, stream);
+}
+
+fa_status fa_fwd_ex(fa_dtype dtype, fa_mask_mode mask_mode, int batch, int n_q_heads,
+                    int n_kv_heads, int seq_len, int head_dim, float scale, const void* q,
+                    const void* k, const void* v, const uint32_t* mask, const uint32_t* tiles,
+                    void* o, float* lse, void* stream) {
+  return run_fwd(dtype, mask_mode, batch, n_q_heads, n_kv_heads, seq_len, head_dim, scale, q, k,
+                 v, mask, tiles, o, lse, stream);
 }
 
 }  // extern "C"

@@ -20,7 +20,7 @@ MODES = {"none": FA_MASK_NONE, "causal": FA_MASK_CAUSAL, "bitmask": FA_MASK_BITM
 DTYPES = {torch.float16: FA_DTYPE_F16, torch.bfloat16: FA_DTYPE_BF16}
 STATUS = {0: "FA_OK", 1: "FA_ERR_NULL_PTR", 2: "FA_ERR_BAD_SHAPE", 3: "FA_ERR_UNSUPPORTED",
           4: "FA_ERR_BAD_MASK_MODE", 5: "FA_ERR_BAD_SCALE", 6: "FA_ERR_HIP"}
-EXPORTS = ("fa_fwd", "fa_fwd_lse", "fa_pack_mask", "fa_mask_tiles", "fa_status_string",
+EXPORTS = ("fa_fwd", "fa_fwd_lse", "fa_fwd_ex", "fa_pack_mask", "fa_mask_tiles", "fa_status_string",
            "fa_abi_version")
 
 _lib = None
@@ -50,6 +50,8 @@ def load() -> ctypes.CDLL:
                                ctypes.c_void_p]
         lib.fa_fwd_lse.restype = ctypes.c_int
         lib.fa_fwd_lse.argtypes = lib.fa_fwd.argtypes[:13] + [ctypes.c_void_p, ctypes.c_void_p]
+        lib.fa_fwd_ex.restype = ctypes.c_int
+        lib.fa_fwd_ex.argtypes = lib.fa_fwd.argtypes[:12] + [ctypes.c_void_p] * 4
         for name in ("fa_pack_mask", "fa_mask_tiles"):
             f = getattr(lib, name)
             f.restype = ctypes.c_int
@@ -81,6 +83,27 @@ def fa_fwd_lse_raw(dtype: int, mask_mode: int, batch: int, n_q_heads: int, n_kv_
     """Direct call of fa_fwd_lse with integer pointers; returns the fa_status code."""
     return load().fa_fwd_lse(dtype, mask_mode, batch, n_q_heads, n_kv_heads, seq_len, head_dim,
                              ctypes.c_float(scale), q, k, v, mask, o, lse, stream)
+
+
+def fa_fwd_ex_raw(dtype: int, mask_mode: int, batch: int, n_q_heads: int, n_kv_heads: int,
+                  seq_len: int, head_dim: int, scale: float, q: int, k: int, v: int, mask: int,
+                  tiles: int, o: int, lse: int, stream: int) -> int:
+    """Direct call of fa_fwd_ex with integer pointers (0 = NULL); returns the fa_status code."""
+    return load().fa_fwd_ex(dtype, mask_mode, batch, n_q_heads, n_kv_heads, seq_len, head_dim,
+                            ctypes.c_float(scale), q, k, v, mask, tiles, o, lse, stream)
+
+
+def _tiles_ptr(tiles, mode, B, Hq, S):
+    if tiles is None:
+        return 0
+    if mode != "bitmask":
+        raise ValueError("a tile summary applies to mode 'bitmask' only")
+    R = (S + 63) // 64
+    shape = (B, Hq, R, (R + 31) // 32)
+    if (tuple(tiles.shape) != shape or tiles.dtype not in (torch.int32, getattr(torch, "uint32", torch.int32))
+            or not tiles.is_cuda or not tiles.is_contiguous()):
+        raise ValueError(f"tiles must be a contiguous 32-bit GPU tensor of shape {shape}")
+    return tiles.data_ptr()
 
 
 def _args(q, k, v, mode, scale, mask, out):
@@ -121,16 +144,23 @@ def _args(q, k, v, mode, scale, mask, out):
 
 def fa_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, mode: str = "none",
            scale: float | None = None, mask: torch.Tensor | None = None,
-           out: torch.Tensor | None = None) -> torch.Tensor:
+           out: torch.Tensor | None = None, tiles: torch.Tensor | None = None) -> torch.Tensor:
     """O = softmax(scale Q K^T + mask) V on the GPU (see include/fa.h for the definition).
 
     q [B,S,Hq,D], k/v [B,S,Hkv,D] (bf16 or fp16, contiguous, on one GPU); mask [B,Hq,S,ceil(S/32)]
-    int32/uint32 words for mode "bitmask".  Enqueued on torch's current stream; returns o."""
+    int32/uint32 words for mode "bitmask"; tiles (optional, bitmask mode) the mask's per-block
+    summary from mask_tiles, so dead 64-key tiles are not loaded.  Enqueued on torch's current
+    stream; returns o."""
     B, S, Hq, Hkv, D, scale, mptr, out = _args(q, k, v, mode, scale, mask, out)
+    tptr = _tiles_ptr(tiles, mode, B, Hq, S)
     stream = torch.cuda.current_stream(q.device).cuda_stream
     with torch.cuda.device(q.device):
-        st = fa_fwd_raw(DTYPES[q.dtype], MODES[mode], B, Hq, Hkv, S, D, scale, q.data_ptr(),
-                        k.data_ptr(), v.data_ptr(), mptr, out.data_ptr(), stream)
+        if tptr:
+            st = fa_fwd_ex_raw(DTYPES[q.dtype], MODES[mode], B, Hq, Hkv, S, D, scale, q.data_ptr(),
+                               k.data_ptr(), v.data_ptr(), mptr, tptr, out.data_ptr(), 0, stream)
+        else:
+            st = fa_fwd_raw(DTYPES[q.dtype], MODES[mode], B, Hq, Hkv, S, D, scale, q.data_ptr(),
+                            k.data_ptr(), v.data_ptr(), mptr, out.data_ptr(), stream)
     if st != 0:
         raise FaError(st, fa_status_string(st))
     return out
@@ -138,11 +168,13 @@ def fa_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, mode: str = "none"
 
 def fa_fwd_lse(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, mode: str = "none",
                scale: float | None = None, mask: torch.Tensor | None = None,
-               out: torch.Tensor | None = None, lse: torch.Tensor | None = None):
+               out: torch.Tensor | None = None, lse: torch.Tensor | None = None,
+               tiles: torch.Tensor | None = None):
     """As fa_fwd, also returning the log-sum-exp of each row's kept scores.
 
     Returns (o, lse) with lse [B, Hq, S] float32 (-inf for a row with no kept key)."""
     B, S, Hq, Hkv, D, scale, mptr, out = _args(q, k, v, mode, scale, mask, out)
+    tptr = _tiles_ptr(tiles, mode, B, Hq, S)
     if lse is None:
         lse = torch.empty((B, Hq, S), dtype=torch.float32, device=q.device)
     elif (tuple(lse.shape) != (B, Hq, S) or lse.dtype != torch.float32 or not lse.is_contiguous()
@@ -150,9 +182,9 @@ def fa_fwd_lse(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, mode: str = "n
         raise ValueError(f"lse must be a contiguous float32 tensor of shape {(B, Hq, S)} on q's device")
     stream = torch.cuda.current_stream(q.device).cuda_stream
     with torch.cuda.device(q.device):
-        st = fa_fwd_lse_raw(DTYPES[q.dtype], MODES[mode], B, Hq, Hkv, S, D, scale, q.data_ptr(),
-                            k.data_ptr(), v.data_ptr(), mptr, out.data_ptr(), lse.data_ptr(),
-                            stream)
+        st = fa_fwd_ex_raw(DTYPES[q.dtype], MODES[mode], B, Hq, Hkv, S, D, scale, q.data_ptr(),
+                           k.data_ptr(), v.data_ptr(), mptr, tptr, out.data_ptr(), lse.data_ptr(),
+                           stream)
     if st != 0:
         raise FaError(st, fa_status_string(st))
     return out, lse

@@ -111,6 +111,26 @@ def empty_tiles(mask: torch.Tensor, tile: int, prob: float, seed: int) -> torch.
     return m
 
 
+def document_mask(mask: torch.Tensor, n_docs: int, seed: int) -> torch.Tensor:
+    """Copy of `mask` restricted to a block diagonal of n_docs documents per batch (a packed
+    batch of sequences: a query sees only keys of its own document).  Document boundaries are
+    drawn at random (seeded); every document holds at least one position."""
+    B, H, S, W = mask.shape
+    assert 1 <= n_docs <= S
+    g = torch.Generator(device="cpu").manual_seed(seed)
+    m = mask.clone()
+    key0 = torch.arange(W, dtype=torch.int64) * 32
+    for b in range(B):
+        cuts = sorted((torch.randperm(S - 1, generator=g)[:n_docs - 1] + 1).tolist())
+        bounds = [0] + cuts + [S]
+        for s0, s1 in zip(bounds[:-1], bounds[1:]):
+            lo = (s0 - key0).clamp(0, 32)
+            hi = (s1 - key0).clamp(0, 32)
+            keep = (torch.ones_like(hi) << hi) - (torch.ones_like(lo) << lo)   # bits [lo, hi)
+            m[b, :, s0:s1, :] &= keep.to(torch.uint32).view(torch.int32)
+    return m
+
+
 # The benchmark grid.  Seed = 1000 * config + variant.
 def tiny_masked() -> Workload:
     return Workload("tiny-masked", "f16", "bitmask", 1, 128, 1, 1, 64, seed=1000)
@@ -119,6 +139,13 @@ def tiny_masked() -> Workload:
 def short_masked(seq_len: int = 512) -> Workload:
     return Workload("short-masked", "f16", "bitmask", 16, seq_len, 16, 16, 64,
                     seed=2000 + (0 if seq_len == 512 else 1))
+
+
+def document_masked(seq_len: int = 1000, n_docs: int = 4) -> Workload:
+    """The short random-mask shape with the mask confined to n_docs packed documents per
+    sequence (random bits inside each document's diagonal block)."""
+    return Workload("document-masked", "f16", "bitmask", 16, seq_len, 16, 16, 64,
+                    seed=2100 + n_docs, extra={"n_docs": n_docs})
 
 
 PREFILL_SHAPES = ((8, 4096), (4, 8192), (2, 16384), (1, 32768))

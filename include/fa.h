@@ -58,7 +58,7 @@
 extern "C" {
 #endif
 
-#define FA_ABI_VERSION 3
+#define FA_ABI_VERSION 4
 
 typedef enum {
   FA_MASK_NONE = 0,     /* every key kept */
@@ -102,6 +102,24 @@ fa_status fa_fwd_lse(fa_dtype dtype, fa_mask_mode mask_mode, int batch, int n_q_
                      int n_kv_heads, int seq_len, int head_dim, float scale, const void* q,
                      const void* k, const void* v, const uint32_t* mask, void* o, float* lse,
                      void* stream);
+
+/* The general form: fa_fwd plus two optional arguments.
+ *   lse    NULL, or as for fa_fwd_lse.
+ *   tiles  NULL, or (FA_MASK_BITMASK only) the per-block summary of `mask` made by
+ *          fa_mask_tiles below ([batch, n_q_heads, R, TW] uint32, R = ceil(seq_len / 64),
+ *          TW = ceil(R / 32), 4-byte aligned DEVICE pointer, R <= 2048).  Each workgroup
+ *          then visits only the 64-key tiles in which some of its rows keep a key, loading no
+ *          K or V for the others -- the tile skip of https://yunpan.plus/t/19526-1-1 section
+ *          "AI生成的代码质量如何？" excerpt 1, taken before the loads.  The summary must cover
+ *          every kept bit of `mask` (fa_mask_tiles' output, or any superset of its set bits):
+ *          keys in tiles it marks empty are treated as masked.  With a valid summary the
+ *          result equals fa_fwd's (bitwise).
+ * Errors as for fa_fwd, plus: tiles with another mask mode -> FA_ERR_BAD_MASK_MODE;
+ * misaligned lse or tiles, or R > 2048, -> FA_ERR_UNSUPPORTED. */
+fa_status fa_fwd_ex(fa_dtype dtype, fa_mask_mode mask_mode, int batch, int n_q_heads,
+                    int n_kv_heads, int seq_len, int head_dim, float scale, const void* q,
+                    const void* k, const void* v, const uint32_t* mask, const uint32_t* tiles,
+                    void* o, float* lse, void* stream);
 
 /* Packs a byte mask into the layout fa_fwd reads in FA_MASK_BITMASK mode.
  *   mask_bytes [batch, n_heads, seq_len, seq_len] uint8, one byte per (query row, key):
