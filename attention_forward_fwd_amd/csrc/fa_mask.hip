@@ -22,6 +22,7 @@ namespace {
 
 using u32 = uint32_t;
 typedef u32 u32x4 __attribute__((ext_vector_type(4)));
+typedef u32 u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kTile = 64;  // summary block: 64 query rows x 64 keys (the attention key tile)
 
@@ -37,7 +38,7 @@ __device__ __forceinline__ u32 low_bits(int n) {
   return n >= 32 ? ~0u : (n <= 0 ? 0u : ((1u << n) - 1u));
 }
 
-// words[row, wi] for every row of the [B*H*S, S] byte matrix.  V = bytes per load (16, 4 or 1):
+// words[row, wi] for every row of the [B*H*S, S] byte matrix.  V = bytes per load (16, 8, 4, 1):
 // the row length and the base address are multiples of V, so full words load in V-byte pieces;
 // the last, partial word of a row (S % 32 != 0) reads only its own bytes.
 template <int V>
@@ -58,6 +59,12 @@ __global__ __launch_bounds__(256) void pack_kernel(const uint8_t* __restrict__ b
 #pragma unroll
       for (int e = 0; e < 4; ++e)
         w |= (nonzero_bytes(a[e]) << (4 * e)) | (nonzero_bytes(b[e]) << (16 + 4 * e));
+    } else if constexpr (V == 8) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const u32x2 a = *(const u32x2*)(src + 8 * e);
+        w |= (nonzero_bytes(a[0]) << (8 * e)) | (nonzero_bytes(a[1]) << (8 * e + 4));
+      }
     } else if constexpr (V == 4) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) w |= nonzero_bytes(*(const u32*)(src + 4 * e)) << (4 * e);
@@ -120,8 +127,11 @@ fa_status fa_pack_mask(int batch, int n_heads, int seq_len, const uint8_t* mask_
   const long long blocks = (n_words + 255) / 256;
   if (blocks >= ((long long)1 << 31)) return FA_ERR_BAD_SHAPE;
   const uintptr_t a = (uintptr_t)mask_bytes;
-  const int v = (seq_len % 16 == 0 && a % 16 == 0) ? 16 : (seq_len % 4 == 0 && a % 4 == 0) ? 4 : 1;
+  const int v = (seq_len % 16 == 0 && a % 16 == 0) ? 16
+                : (seq_len % 8 == 0 && a % 8 == 0) ? 8
+                : (seq_len % 4 == 0 && a % 4 == 0) ? 4 : 1;
   const void* k = v == 16 ? (const void*)pack_kernel<16>
+                  : v == 8 ? (const void*)pack_kernel<8>
                   : v == 4 ? (const void*)pack_kernel<4>
                            : (const void*)pack_kernel<1>;
   int S = seq_len, Wa = W;

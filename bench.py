@@ -5,8 +5,11 @@ One step = one fa_fwd launch over the whole workload (every row tile, every head
 batch), inputs already resident in device memory.  Default workload: non-causal MHA prefill,
 bf16, head dim 128, 16 heads, batch 4 x 8192 tokens (the 32768-token prefill grid of
 https://yetianai.com/news/16520, section "七天跑出的成绩单").  The causal variant of the same
-shape and every other workload of the grid (other sequence lengths, GQA, the short random-mask
-cases) are timed alongside and reported under "also".
+shape, every other workload of the grid (other sequence lengths, GQA, the short random-mask
+cases), the default workload through fa_fwd_lse (O plus the per-row log-sum-exp) and the mask
+kernels (byte-mask packing and the tile summary, on the B16 H16 S1000 shape) and a packed-document
+mask on that shape (dense walk vs the tile-summary walk) are timed alongside and reported under
+"also".
 
 Prints ONE JSON line.  FLOPs are counted dense, 4*B*Hq*S^2*d, half of that for causal.
 """
@@ -95,6 +98,60 @@ def time_grid(fa_fwd, inputs, dev, main, steps):
     return out
 
 
+def time_mask_kernels(inputs, dev, steps):
+    """fa_pack_mask and fa_mask_tiles on the short random-mask shape (B16 H16 S1000): HBM-bound,
+    reported as algorithmic bytes per second (bytes read once + words written once)."""
+    import torch
+    from attention_forward_fwd_amd import mask_tiles, pack_mask
+    w = inputs.short_masked(1000)
+    B, H, S = w.batch, w.n_q_heads, w.seq_len
+    W, R = (S + 31) // 32, (S + 63) // 64
+    g = torch.Generator(device=dev)
+    g.manual_seed(w.seed + 90)
+    mbytes = (torch.rand((B, H, S, S), generator=g, device=dev) < 0.5).to(torch.uint8)
+    words = torch.empty((B, H, S, W), dtype=torch.int32, device=dev)
+    tiles = torch.empty((B, H, R, (R + 31) // 32), dtype=torch.int32, device=dev)
+    out = {}
+    for name, fn, nbytes in (
+            ("fa_pack_mask", lambda: pack_mask(mbytes, out=words), B * H * S * S + words.numel() * 4),
+            ("fa_mask_tiles", lambda: mask_tiles(words, out=tiles), words.numel() * 4 + tiles.numel() * 4)):
+        ms = time_launches(fn, steps, 3)
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        out[f"{name} B{B} H{H} S{S}"] = {"us": ms * 1e3, "alg_bytes": nbytes, "hbm_gbs": gbs,
+                                         "frac_of_hbm": gbs / PEAK_HBM_GBS}
+    del mbytes, words, tiles
+    return out
+
+
+def time_document_mask(inputs, dev, steps):
+    """Packed documents (4 per sequence) on the short random-mask shape: the dense walk (every
+    key tile loaded, dead ones skipped by the wave ballot) against the walk over the tiles the
+    mask's summary marks live (dead tiles neither loaded nor visited).  The summary itself is
+    made once per mask (fa_mask_tiles, timed with the mask kernels)."""
+    import torch
+    from attention_forward_fwd_amd import fa_fwd, mask_tiles
+    w = inputs.document_masked(1000, 4)
+    q, k, v = inputs.make_qkv_device(w, dev)
+    m = inputs.document_mask(inputs.make_bitmask(w), w.extra["n_docs"], seed=w.seed + 1).to(dev)
+    tiles = mask_tiles(m)
+    o = torch.empty_like(q)
+    f = flops(w.batch, w.n_q_heads, w.seq_len, w.head_dim, w.mode)
+    out = {}
+    for name, kw in (("dense walk", {}), ("tile walk", {"tiles": tiles})):
+        ms = time_launches(lambda: fa_fwd(q, k, v, mode="bitmask", scale=w.scale, mask=m, out=o, **kw),
+                           steps, 3)
+        out[f"{w.label} {name}"] = {"us": ms * 1e3, "dense_equivalent_tflops": f / (ms * 1e-3) / 1e12,
+                                     "live_tile_fraction": None}
+    # fraction of (row block, key tile) pairs the summary marks live
+    t = tiles.cpu().numpy().view("uint32")
+    R = (w.seq_len + 63) // 64
+    bits = sum(bin(int(x)).count("1") for x in t.ravel())
+    for rec in out.values():
+        rec["live_tile_fraction"] = bits / (w.batch * w.n_q_heads * R * R)
+    del q, k, v, m, tiles, o
+    return out
+
+
 def cpu_baseline(w, q, k, v, mask, o_gpu, budget_s):
     """Time the fp64 oracle on a bounded sample of the same workload (row blocks of one head
     at full key length, as many as fit in budget_s) and check the GPU rows it covers."""
@@ -175,7 +232,7 @@ def main():
         sys.exit(2)
 
     import torch
-    from attention_forward_fwd_amd import fa_fwd, inputs
+    from attention_forward_fwd_amd import fa_fwd, fa_fwd_lse, inputs
 
     dev = torch.device("cuda:0")
     seq_len = args.seq_len or (512 if args.workload == "short-masked" else 8192)
@@ -204,6 +261,17 @@ def main():
     o_main = out.clone()
 
     also = {} if args.no_also else time_grid(fa_fwd, inputs, dev, w, max(5, args.steps // 2))
+    if not args.no_also:
+        # The same workload through fa_fwd_lse (O plus each row's log-sum-exp).
+        lse = torch.empty((w.batch, w.n_q_heads, w.seq_len), dtype=torch.float32, device=dev)
+        ms_lse = time_launches(lambda: fa_fwd_lse(qd, kd, vd, mode=w.mode, scale=w.scale,
+                                                  mask=maskd, out=out, lse=lse),
+                               max(5, args.steps // 2), 3)
+        also["fa_fwd_lse " + w.label] = {"ms": ms_lse, "tflops": f / (ms_lse * 1e-3) / 1e12,
+                                         "frac_of_peak": f / (ms_lse * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
+        del lse
+        also.update(time_mask_kernels(inputs, dev, 50))
+        also.update(time_document_mask(inputs, dev, 100))
 
     bytes_alg = alg_bytes(w)   # Q, K, V (and mask) read + O written
     # HBM bytes per launch measured with rocprofv3 byte counters (profiles/traffic.json); only

@@ -1,5 +1,5 @@
 """GPU parity of the mask kernels (fa_pack_mask, fa_mask_tiles) against the CPU oracle: bit-exact
-on every output word, for ragged lengths, every load width the packer picks (16-, 4- and
+on every output word, for ragged lengths, every load width the packer picks (16-, 8-, 4- and
 1-byte pieces, from the row length and the base alignment), value spreads, structured masks,
 the short random-mask benchmark size, and guard bands around the outputs."""
 
@@ -33,8 +33,8 @@ def _gpu_pack(b_np, offset=0):
     return w.cpu().numpy().view(np.uint32)
 
 
-@pytest.mark.parametrize("offset", [0, 4, 1])
-@pytest.mark.parametrize("S", [1, 7, 31, 32, 33, 100, 128, 1000, 1025])
+@pytest.mark.parametrize("offset", [0, 8, 4, 1])
+@pytest.mark.parametrize("S", [1, 7, 31, 32, 33, 100, 128, 136, 1000, 1025])
 def test_pack_ragged_and_alignment(S, offset):
     b = _bytes(400 + S + offset, (2, 3, S, S))
     log(f"case pack S={S} offset={offset}")
