@@ -8,9 +8,9 @@
 //   clear, which the summary lets a caller (or a later pass) see per 64 x 64 block.
 //
 // Both kernels are bound by HBM bandwidth (a byte per (query, key) read once, an eighth of that
-// written; the summary reads the words once), so they are written for full-line coalesced
-// traffic and little else: one thread per output word, consecutive threads on consecutive
-// words of a row.
+// written; the summary reads the words once), so they are written for coalesced traffic: one
+// wave per run of 64 words of a row, each load instruction covering 512 B - 1 KiB of
+// consecutive bytes, and the words assembled across lanes with shuffles.
 
 #include <hip/hip_runtime.h>
 #include <stddef.h>
@@ -38,6 +38,69 @@ __device__ __forceinline__ u32 low_bits(int n) {
   return n >= 32 ? ~0u : (n <= 0 ? 0u : ((1u << n) - 1u));
 }
 
+// Each wave takes IPW consecutive items, an item being one (row, run of 64 words).  Load e of
+// lane l reads the V (16 or 8) bytes at row offset 2048 seg + 64 V e + V l, so every load
+// instruction covers 64 V consecutive bytes; all loads of the wave's items are issued before
+// any result is used.  Those bytes are part l % (32 / V) of word 64 seg + (64 V / 32) e +
+// l / (32 / V); the lane keeps the piece's V bits at bit V e of its value, and lane j then
+// gathers the 32 / V parts of word 64 seg + j from the lanes that loaded them.  The row length
+// S and the base address are multiples of V, so a piece never straddles the row end; pieces
+// past it are 0 (padding bits).
+constexpr int kItemsPerWave = 4;
+template <int V>
+__global__ __launch_bounds__(256) void pack_rows_kernel(const uint8_t* __restrict__ bytes,
+                                                        u32* __restrict__ words, int S, int W,
+                                                        int n_seg, long long n_items) {
+  static_assert(V == 16 || V == 8, "piece size");
+  constexpr int PARTS = 32 / V;   // pieces per word
+  constexpr int LOADS = 32 / V;   // load instructions per 2 KiB run (64 words)
+  constexpr int IPW = kItemsPerWave;
+  const long long item0 = ((long long)blockIdx.x * 4 + (threadIdx.x >> 6)) * IPW;
+  const int lane = threadIdx.x & 63;
+  if (item0 >= n_items) return;  // (whole waves)
+  u32 v[IPW];
+#pragma unroll
+  for (int it = 0; it < IPW; ++it) {
+    v[it] = 0u;
+    const long long item = item0 + it;
+    if (item < n_items) {
+      const long long row = item / n_seg;
+      const int seg = (int)(item - row * n_seg);
+      const uint8_t* rb = bytes + row * (long long)S;
+#pragma unroll
+      for (int e = 0; e < LOADS; ++e) {
+        const int col = 2048 * seg + 64 * V * e + V * lane;
+        if (col < S) {
+          if constexpr (V == 16) {
+            const u32x4 a = *(const u32x4*)(rb + col);
+            v[it] |= (nonzero_bytes(a[0]) | (nonzero_bytes(a[1]) << 4) |
+                      (nonzero_bytes(a[2]) << 8) | (nonzero_bytes(a[3]) << 12)) << (16 * e);
+          } else {
+            const u32x2 a = *(const u32x2*)(rb + col);
+            v[it] |= (nonzero_bytes(a[0]) | (nonzero_bytes(a[1]) << 4)) << (8 * e);
+          }
+        }
+      }
+    }
+  }
+  // word 64 seg + j: load e = j / (64 / PARTS), parts from lanes PARTS (j % (64 / PARTS)) + k
+  const int j = lane, e = j / (64 / PARTS), src = PARTS * (j % (64 / PARTS));
+#pragma unroll
+  for (int it = 0; it < IPW; ++it) {
+    u32 w = 0u;
+#pragma unroll
+    for (int k = 0; k < PARTS; ++k)
+      w |= ((__shfl((int)v[it], src + k) >> (V * e)) & ((1u << V) - 1u)) << (V * k);
+    const long long item = item0 + it;
+    if (item < n_items) {
+      const long long row = item / n_seg;
+      const int wi = 64 * (int)(item - row * n_seg) + j;
+      if (wi < W) words[row * W + wi] = w;
+    }
+  }
+}
+
+// Fallback (row length or base not a multiple of 8): one thread per word.
 // words[row, wi] for every row of the [B*H*S, S] byte matrix.  V = bytes per load (16, 8, 4, 1):
 // the row length and the base address are multiples of V, so full words load in V-byte pieces;
 // the last, partial word of a row (S % 32 != 0) reads only its own bytes.
@@ -78,35 +141,43 @@ __global__ __launch_bounds__(256) void pack_kernel(const uint8_t* __restrict__ b
   words[gid] = w;
 }
 
-// tiles[bh, r, t / 32] bit t % 32 = any kept bit in rows [64r, 64r+64) x keys [64t, 64t+64) of
-// head bh, bits at keys >= S ignored.  One thread per (bh, r, t) with t over TW * 32 slots, so
-// each aligned 32-lane half of a wave owns one summary word, assembled with a ballot.
+// tiles[bh, r, c] bit i = any kept bit in rows [64r, 64r+64) x keys [64t, 64t+64) of head bh,
+// t = 32 c + i, bits at keys >= S ignored.  One wave per (bh, r, c): lane l ORs word 64 c + l of
+// the block's rows (one 256-byte load instruction per row), a ballot marks the nonzero words,
+// and tile t is the OR of the bits of its two words 2t, 2t+1.
 __global__ __launch_bounds__(256) void tiles_kernel(const u32* __restrict__ words,
                                                     u32* __restrict__ tiles, int S, int W,
-                                                    int n_rb, int TW, long long n_items) {
-  const long long gid = (long long)blockIdx.x * 256 + threadIdx.x;
-  bool any = false;
-  if (gid < n_items) {
-    const int slots = TW * 32;
-    const long long rbh = gid / slots;
-    const int t = (int)(gid - rbh * slots);
-    const int r = (int)(rbh % n_rb);
-    const long long bh = rbh / n_rb;
-    if (t < n_rb) {  // (as many key tiles as row blocks: the mask is square)
-      const u32* base = words + (bh * S + (long long)kTile * r) * W + 2 * t;
-      const int rows = min(kTile, S - kTile * r);
-      const u32 m0 = low_bits(S - kTile * t), m1 = low_bits(S - kTile * t - 32);
-      u32 acc = 0u;
-      if (m1) {
-        for (int i = 0; i < rows; ++i) acc |= (base[(long long)i * W] & m0) | (base[(long long)i * W + 1] & m1);
-      } else {
-        for (int i = 0; i < rows; ++i) acc |= base[(long long)i * W] & m0;
-      }
-      any = acc != 0u;
+                                                    int n_rb, int TW, long long n_waves) {
+  const long long wv = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (wv >= n_waves) return;  // (whole waves)
+  const long long rbh = wv / TW;
+  const int c = (int)(wv - rbh * TW);
+  const int r = (int)(rbh % n_rb);
+  const long long bh = rbh / n_rb;
+  const int wi = 64 * c + lane;
+  u32 acc = 0u;
+  if (wi < W) {
+    const u32 valid = low_bits(S - 32 * wi);
+    const u32* col = words + (bh * S + (long long)kTile * r) * W + wi;
+    const int rows = min(kTile, S - kTile * r);
+    int i = 0;
+    for (; i + 8 <= rows; i += 8) {
+#pragma unroll
+      for (int u = 0; u < 8; ++u) acc |= col[(long long)(i + u) * W];
     }
+    for (; i < rows; ++i) acc |= col[(long long)i * W];
+    acc &= valid;
   }
-  const unsigned long long bal = __ballot(any);
-  if (gid < n_items && (threadIdx.x & 31) == 0) tiles[gid >> 5] = (u32)(bal >> (threadIdx.x & 32));
+  unsigned long long x = __ballot(acc != 0u);
+  // tile i of the run = word bits 2i | 2i+1, compacted to bit i
+  x = (x | (x >> 1)) & 0x5555555555555555ull;
+  x = (x | (x >> 1)) & 0x3333333333333333ull;
+  x = (x | (x >> 2)) & 0x0f0f0f0f0f0f0f0full;
+  x = (x | (x >> 4)) & 0x00ff00ff00ff00ffull;
+  x = (x | (x >> 8)) & 0x0000ffff0000ffffull;
+  x = (x | (x >> 16)) & 0x00000000ffffffffull;
+  if (lane == 0) tiles[rbh * TW + c] = (u32)x;
 }
 
 bool shape_ok(int batch, int n_heads, int seq_len) {
@@ -127,17 +198,25 @@ fa_status fa_pack_mask(int batch, int n_heads, int seq_len, const uint8_t* mask_
   const long long blocks = (n_words + 255) / 256;
   if (blocks >= ((long long)1 << 31)) return FA_ERR_BAD_SHAPE;
   const uintptr_t a = (uintptr_t)mask_bytes;
-  const int v = (seq_len % 16 == 0 && a % 16 == 0) ? 16
-                : (seq_len % 8 == 0 && a % 8 == 0) ? 8
-                : (seq_len % 4 == 0 && a % 4 == 0) ? 4 : 1;
-  const void* k = v == 16 ? (const void*)pack_kernel<16>
-                  : v == 8 ? (const void*)pack_kernel<8>
-                  : v == 4 ? (const void*)pack_kernel<4>
-                           : (const void*)pack_kernel<1>;
   int S = seq_len, Wa = W;
-  long long nw = n_words;
-  void* args[] = {(void*)&mask_bytes, (void*)&mask_words, (void*)&S, (void*)&Wa, (void*)&nw};
-  const hipError_t e = hipLaunchKernel(k, dim3((unsigned)blocks), dim3(256), args, 0, (hipStream_t)stream);
+  hipError_t e;
+  if (seq_len % 8 == 0 && a % 8 == 0) {  // wave per 64-word run, contiguous loads
+    int n_seg = (W + 63) / 64;
+    long long n_items = (long long)batch * n_heads * seq_len * n_seg;
+    const long long wblocks = (n_items + 4 * kItemsPerWave - 1) / (4 * kItemsPerWave);
+    if (wblocks >= ((long long)1 << 31)) return FA_ERR_BAD_SHAPE;
+    const void* k = (seq_len % 16 == 0 && a % 16 == 0) ? (const void*)pack_rows_kernel<16>
+                                                        : (const void*)pack_rows_kernel<8>;
+    void* args[] = {(void*)&mask_bytes, (void*)&mask_words, (void*)&S, (void*)&Wa, (void*)&n_seg,
+                    (void*)&n_items};
+    e = hipLaunchKernel(k, dim3((unsigned)wblocks), dim3(256), args, 0, (hipStream_t)stream);
+  } else {
+    const void* k = (seq_len % 4 == 0 && a % 4 == 0) ? (const void*)pack_kernel<4>
+                                                      : (const void*)pack_kernel<1>;
+    long long nw = n_words;
+    void* args[] = {(void*)&mask_bytes, (void*)&mask_words, (void*)&S, (void*)&Wa, (void*)&nw};
+    e = hipLaunchKernel(k, dim3((unsigned)blocks), dim3(256), args, 0, (hipStream_t)stream);
+  }
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
@@ -149,12 +228,12 @@ fa_status fa_mask_tiles(int batch, int n_heads, int seq_len, const uint32_t* mas
   const int W = (seq_len + 31) / 32;
   const int n_rb = (seq_len + kTile - 1) / kTile;
   const int TW = (n_rb + 31) / 32;
-  const long long n_items = (long long)batch * n_heads * n_rb * TW * 32;
-  const long long blocks = (n_items + 255) / 256;
+  const long long n_waves = (long long)batch * n_heads * n_rb * TW;
+  const long long blocks = (n_waves + 3) / 4;
   if (blocks >= ((long long)1 << 31)) return FA_ERR_BAD_SHAPE;
   int S = seq_len, Wa = W, nrb = n_rb, tw = TW;
-  long long ni = n_items;
-  void* args[] = {(void*)&mask_words, (void*)&tiles, (void*)&S, (void*)&Wa, (void*)&nrb, (void*)&tw, (void*)&ni};
+  long long nwv = n_waves;
+  void* args[] = {(void*)&mask_words, (void*)&tiles, (void*)&S, (void*)&Wa, (void*)&nrb, (void*)&tw, (void*)&nwv};
   const hipError_t e = hipLaunchKernel((const void*)tiles_kernel, dim3((unsigned)blocks), dim3(256),
                                        args, 0, (hipStream_t)stream);
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
