@@ -53,6 +53,7 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <algorithm>
 #include <mutex>
 #include <type_traits>
 
@@ -84,6 +85,10 @@ struct Params {
   const u32* tiles;  // bitmask mode: [B, Hq, n_rb, TW] summary of 64x64 blocks with a kept bit,
                      // or null (then every key tile is visited)
   int n_rb, TW;      // 64-row blocks per head, summary words per block
+  int n_split;       // key ranges each row tile is split into (1 = none)
+  float* o_part;     // n_split > 1: [n_split, B*S*Hq, D] unnormalised fp32 O of each key range
+  float* ml_part;    // n_split > 1: [n_split, B*S*Hq, 2] running max and row sum of each range
+  size_t part_rows;  // B*S*Hq
   int S, Hq, Hkv, G, W;
   int n_kt;   // 64-key tiles per sequence
   int n_rt;   // row tiles per (batch, kv head)
@@ -104,6 +109,8 @@ constexpr int kWideRows = 8192;   // rows per KV head (S x G) from which it is u
 constexpr int kWideRowsCausal = 16384;  // (causal: its longer tail pays off later)
 constexpr int kPackRowTiles = 8;  // row tiles per KV head from which V is packed once up front
 constexpr int kMaxListTiles = 2048;  // key tiles a workgroup can list from a tile summary
+constexpr int kMaxSplits = 16;       // key ranges per row tile (split-KV)
+constexpr int kNumCUs = 256;         // MI355X compute units (automatic split-KV sizing)
 #ifndef FA_P1_VALU
 #define FA_P1_VALU 8
 #endif
@@ -406,6 +413,12 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void fa_fwd_kernel(Params
       wg = x * q8 + min(x, r8) + idx;
     }
   }
+  // Split-KV: the key ranges of one row tile are consecutive logical workgroups (same XCD).
+  int split = 0;
+  if (p.n_split > 1) {
+    split = wg % p.n_split;
+    wg /= p.n_split;
+  }
   const int bh = wg / p.n_rt;
   int rt = wg - bh * p.n_rt;
   if (MODE == kCausal) rt = p.n_rt - 1 - rt;  // longest causal rows first
@@ -471,21 +484,41 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void fa_fwd_kernel(Params
       n_tiles = __builtin_amdgcn_readfirstlane(tcount);
     }
   }
+  // Split-KV (never with a tile summary): key range `split` of n_split equal shares of this
+  // workgroup's tiles.
+  int kt0 = 0;
+  if (p.n_split > 1) {
+    const int chunk = (n_tiles + p.n_split - 1) / p.n_split;
+    kt0 = split * chunk;
+    n_tiles = max(0, min(n_tiles - kt0, chunk));
+  }
   auto tix = [&](int j) __attribute__((always_inline)) {
     const int jj = min(j, n_tiles - 1);
     if constexpr (MODE == kBitmask) {
       if (sparse) return __builtin_amdgcn_readfirstlane((int)tlist[jj]);
     }
-    return jj;
+    return kt0 + jj;
   };
-  if (n_tiles == 0) {  // (tile summary) no key of these rows is kept: O = 0, LSE = -inf
+  // Row index of O (and of the split partials): (b, position, query head), token-major.
+  const size_t orow_idx = ((size_t)b * S + my_pos) * Hq + my_head;
+  if (n_tiles == 0) {  // (tile summary or an empty key range) no key of these rows is visited
     if (wave_live && my_pos < S) {
-      uint16_t* orow = p.o + q_batch + ((size_t)my_pos * Hq + my_head) * D;
+      if (p.n_split > 1) {  // empty partial: max at the floor, sum 0, O 0
+        float* op = p.o_part + ((size_t)split * p.part_rows + orow_idx) * D;
 #pragma unroll
-      for (int db = 0; db < D / 32; ++db)
+        for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-        for (int t4 = 0; t4 < 4; ++t4) *(u32x2*)(orow + 32 * db + 8 * t4 + 4 * hl) = (u32x2){0u, 0u};
-      if (p.lse && hl == 0) p.lse[((size_t)b * Hq + my_head) * S + my_pos] = -INFINITY;
+          for (int t4 = 0; t4 < 4; ++t4) *(f32x4*)(op + 32 * db + 8 * t4 + 4 * hl) = (f32x4){0.f, 0.f, 0.f, 0.f};
+        if (hl == 0)
+          *(float2*)(p.ml_part + ((size_t)split * p.part_rows + orow_idx) * 2) = make_float2(-1e30f, 0.f);
+      } else {
+        uint16_t* orow = p.o + q_batch + ((size_t)my_pos * Hq + my_head) * D;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+          for (int t4 = 0; t4 < 4; ++t4) *(u32x2*)(orow + 32 * db + 8 * t4 + 4 * hl) = (u32x2){0u, 0u};
+        if (p.lse && hl == 0) p.lse[((size_t)b * Hq + my_head) * S + my_pos] = -INFINITY;
+      }
     }
     return;
   }
@@ -879,6 +912,23 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void fa_fwd_kernel(Params
 
   // ---- Epilogue: O / l (0 for a row with no kept key), rounded, 8-byte stores.
   const float lt = sum_halves(l_run);
+  if (p.n_split > 1) {  // split-KV: this key range's unnormalised O, running max and row sum
+    if (wave_live && my_pos < S) {
+      float* op = p.o_part + ((size_t)split * p.part_rows + orow_idx) * D;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int t4 = 0; t4 < 4; ++t4) {
+          f32x4 x;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) x[e] = oacc[db][4 * t4 + e];
+          *(f32x4*)(op + 32 * db + 8 * t4 + 4 * hl) = x;
+        }
+      if (hl == 0)
+        *(float2*)(p.ml_part + ((size_t)split * p.part_rows + orow_idx) * 2) = make_float2(m_run, lt);
+    }
+    return;
+  }
   const float inv = lt > 0.f ? __builtin_amdgcn_rcpf(lt) : 0.f;
   if (wave_live && my_pos < S) {
     uint16_t* orow = p.o + q_batch + ((size_t)my_pos * Hq + my_head) * D;
@@ -899,6 +949,60 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void fa_fwd_kernel(Params
       p.lse[((size_t)b * Hq + my_head) * S + my_pos] =
           lt > 0.f ? (m_run + __builtin_amdgcn_logf(lt)) * 0.693147180559945f : -INFINITY;
   }
+}
+
+// Split-KV merge: for each row, the key ranges' states (m_s, l_s, O_s), with O_s summed from
+// weights 2^(s c - m_s), combine exactly as the online softmax combines tiles:
+// m = max m_s, l = sum 2^(m_s - m) l_s, O = sum 2^(m_s - m) O_s / l (0 when l = 0), and
+// lse = (m + log2 l) ln 2.  One thread per 4 consecutive elements of a row.
+template <bool BF16, int D>
+__global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ o_part,
+                                                    const float* __restrict__ ml_part,
+                                                    uint16_t* __restrict__ o, float* __restrict__ lse,
+                                                    int n_split, size_t rows, int S, int Hq) {
+  constexpr int TPR = D / 4;  // threads per row
+  const size_t gid = (size_t)blockIdx.x * 256 + threadIdx.x;
+  const size_t row = gid / TPR;
+  const int c = (int)(gid - row * TPR);
+  if (row >= rows) return;
+  float m = -1e30f;
+  for (int s = 0; s < n_split; ++s) m = fmaxf(m, ml_part[((size_t)s * rows + row) * 2]);
+  float l = 0.f;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int s = 0; s < n_split; ++s) {
+    const float2 ml = *(const float2*)(ml_part + ((size_t)s * rows + row) * 2);
+    const float w = __builtin_amdgcn_exp2f(ml.x - m);
+    l += w * ml.y;
+    const f32x4 x = *(const f32x4*)(o_part + ((size_t)s * rows + row) * D + 4 * c);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc[e] += w * x[e];
+  }
+  const float inv = l > 0.f ? __builtin_amdgcn_rcpf(l) : 0.f;
+  f32x4 y;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) y[e] = acc[e] * inv;
+  *(u32x2*)(o + row * D + 4 * c) = pack4<BF16>(y);
+  if (lse && c == 0) {
+    const size_t sh = (size_t)S * Hq;
+    const size_t bb = row / sh, rem = row - bb * sh;
+    const size_t pos = rem / Hq, h = rem - pos * Hq;
+    lse[(bb * Hq + h) * S + pos] =
+        l > 0.f ? (m + __builtin_amdgcn_logf(l)) * 0.693147180559945f : -INFINITY;
+  }
+}
+
+template <bool BF16, int D>
+hipError_t launch_merge(const Params& p, float* lse, hipStream_t s) {
+  const float* op = p.o_part;
+  const float* ml = p.ml_part;
+  uint16_t* o = p.o;
+  int n_split = p.n_split, S = p.S, Hq = p.Hq;
+  size_t rows = p.part_rows;
+  void* args[] = {(void*)&op, (void*)&ml, (void*)&o, (void*)&lse, (void*)&n_split, (void*)&rows,
+                  (void*)&S, (void*)&Hq};
+  const size_t blocks = (rows * (D / 4) + 255) / 256;
+  return hipLaunchKernel((const void*)merge_kernel<BF16, D>, dim3((unsigned)blocks), dim3(256),
+                         args, 0, s);
 }
 
 // Instances: 4 waves with or without packed V, 8 waves with packed V (a KV head with that many
@@ -990,7 +1094,7 @@ namespace {
 fa_status run_fwd(fa_dtype dtype, fa_mask_mode mask_mode, int batch, int n_q_heads,
                   int n_kv_heads, int seq_len, int head_dim, float scale, const void* q,
                   const void* k, const void* v, const uint32_t* mask, const uint32_t* tiles,
-                  void* o, float* lse, void* stream) {
+                  int kv_splits, void* o, float* lse, void* stream) {
   if (dtype != FA_DTYPE_F16 && dtype != FA_DTYPE_BF16) return FA_ERR_UNSUPPORTED;
   if (mask_mode != FA_MASK_NONE && mask_mode != FA_MASK_CAUSAL && mask_mode != FA_MASK_BITMASK)
     return FA_ERR_BAD_MASK_MODE;
@@ -1021,6 +1125,18 @@ fa_status run_fwd(fa_dtype dtype, fa_mask_mode mask_mode, int batch, int n_q_hea
     if (mask_mode != FA_MASK_BITMASK) return FA_ERR_BAD_MASK_MODE;
     if (((uintptr_t)tiles & 3u) || n_rb > kMaxListTiles) return FA_ERR_UNSUPPORTED;
   }
+  if (kv_splits < 0 || kv_splits > kMaxSplits || (tiles && kv_splits > 1)) return FA_ERR_UNSUPPORTED;
+  // Split-KV: explicit, or (kv_splits == 0, no tile summary) when the grid fills at most half
+  // of the chip's workgroup slots (one 256-row or two 128-row workgroups per CU): enough key
+  // ranges per row tile to fill it, each at least 8 tiles long.
+  int n_split = kv_splits > 1 ? min(kv_splits, n_kt) : 1;
+  if (kv_splits == 0 && !tiles) {
+    const int64_t slots = nw == kWide ? kNumCUs : 2 * kNumCUs;
+    if (2 * n_wg <= slots)
+      n_split = (int)std::min<int64_t>({(int64_t)kMaxSplits, (slots + n_wg - 1) / n_wg,
+                                        std::max<int64_t>(1, n_kt / 8)});
+  }
+  if (n_wg * n_split >= ((int64_t)1 << 31)) return FA_ERR_BAD_SHAPE;
 
   Params p;
   p.q = (const uint16_t*)q;
@@ -1038,13 +1154,18 @@ fa_status run_fwd(fa_dtype dtype, fa_mask_mode mask_mode, int batch, int n_q_hea
   p.G = G;
   p.W = (seq_len + 31) / 32;
   p.n_rt = (int)n_rt;
-  p.n_wg = (int)n_wg;
+  p.n_wg = (int)(n_wg * n_split);  // the grid (key ranges of one row tile are adjacent)
+  p.n_split = n_split;
+  p.part_rows = (size_t)batch * seq_len * n_q_heads;
+  p.o_part = nullptr;
+  p.ml_part = nullptr;
   p.n_kt = n_kt;
   p.vt = nullptr;
   // Causal balance across the 8 XCDs: when the grid is a multiple of 8 and one head's row tiles
   // fill exactly k > 1 XCDs' shares, the kernel deals each head's tiles over its k XCDs.
   p.xsplit = 0;
-  if (n_wg % 8 == 0 && n_rt % (n_wg / 8) == 0 && n_rt > n_wg / 8) p.xsplit = (int)(n_rt / (n_wg / 8));
+  if (n_split == 1 && n_wg % 8 == 0 && n_rt % (n_wg / 8) == 0 && n_rt > n_wg / 8)
+    p.xsplit = (int)(n_rt / (n_wg / 8));
   // exp(x) = 2^(x log2 e): fold log2(e) into the scale.  A zero scale becomes a tiny positive
   // one (2^-100): every 2^(s*c - m) is then 1 to fp32 precision, the uniform average the zero
   // scale defines, without 0 * inf on masked scores.
@@ -1057,18 +1178,29 @@ fa_status run_fwd(fa_dtype dtype, fa_mask_mode mask_mode, int batch, int n_q_hea
   // by kPackRowTiles or more row-tile workgroups (always so for the 256-row workgroup).
   const bool vpack = pack_ok && (nw == kWide || n_rt >= kPackRowTiles);
   hipError_t e = hipSuccess;
-  void* ws = nullptr;
-  if (vpack) {
-    hipMemPool_t pool;
+  void* ws = nullptr;    // packed V^T
+  void* part = nullptr;  // split-KV partials
+  hipMemPool_t pool = nullptr;
+  if (vpack || n_split > 1) {
     e = workspace_pool(&pool);
-    if (e == hipSuccess)
-      e = hipMallocFromPoolAsync(&ws, (size_t)batch * n_kv_heads * p.n_kt * tile_bytes, pool, s);
     if (e != hipSuccess) return FA_ERR_HIP;
-    p.vt = (const uint16_t*)ws;
-    e = head_dim == 128 ? launch_pack<128>(p, batch, s) : launch_pack<64>(p, batch, s);
   }
+  if (n_split > 1) {
+    e = hipMallocFromPoolAsync(&part, (size_t)n_split * p.part_rows * (head_dim + 2) * 4, pool, s);
+    if (e != hipSuccess) return FA_ERR_HIP;
+    p.o_part = (float*)part;
+    p.ml_part = p.o_part + (size_t)n_split * p.part_rows * head_dim;
+    p.lse = nullptr;  // (written by the merge)
+  }
+  if (vpack) {
+    e = hipMallocFromPoolAsync(&ws, (size_t)batch * n_kv_heads * p.n_kt * tile_bytes, pool, s);
+    if (e == hipSuccess) {
+      p.vt = (const uint16_t*)ws;
+      e = head_dim == 128 ? launch_pack<128>(p, batch, s) : launch_pack<64>(p, batch, s);
+    }
+  }
+  const bool bf16 = dtype == FA_DTYPE_BF16;
   if (e == hipSuccess) {
-    const bool bf16 = dtype == FA_DTYPE_BF16;
     if (bf16)
       e = head_dim == 128 ? launch_mode<true, 128>(mask_mode, p, vpack, nw, s)
                           : launch_mode<true, 64>(mask_mode, p, vpack, nw, s);
@@ -1076,9 +1208,17 @@ fa_status run_fwd(fa_dtype dtype, fa_mask_mode mask_mode, int batch, int n_q_hea
       e = head_dim == 128 ? launch_mode<false, 128>(mask_mode, p, vpack, nw, s)
                           : launch_mode<false, 64>(mask_mode, p, vpack, nw, s);
   }
-  if (ws) {
-    const hipError_t ef = hipFreeAsync(ws, s);
-    if (e == hipSuccess) e = ef;
+  if (e == hipSuccess && n_split > 1) {
+    if (bf16)
+      e = head_dim == 128 ? launch_merge<true, 128>(p, lse, s) : launch_merge<true, 64>(p, lse, s);
+    else
+      e = head_dim == 128 ? launch_merge<false, 128>(p, lse, s) : launch_merge<false, 64>(p, lse, s);
+  }
+  for (void* buf : {ws, part}) {
+    if (buf) {
+      const hipError_t ef = hipFreeAsync(buf, s);
+      if (e == hipSuccess) e = ef;
+    }
   }
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
@@ -1091,7 +1231,7 @@ fa_status fa_fwd(fa_dtype dtype, fa_mask_mode mask_mode, int batch, int n_q_head
                  int n_kv_heads, int seq_len, int head_dim, float scale, const void* q,
                  const void* k, const void* v, const uint32_t* mask, void* o, void* stream) {
   return run_fwd(dtype, mask_mode, batch, n_q_heads, n_kv_heads, seq_len, head_dim, scale, q, k,
-                 v, mask, nullptr, o, nullptr, stream);
+                 v, mask, nullptr, 1, o, nullptr, stream);
 }
 
 fa_status fa_fwd_lse(fa_dtype dtype, fa_mask_mode mask_mode, int batch, int n_q_heads,
@@ -1100,15 +1240,15 @@ fa_status fa_fwd_lse(fa_dtype dtype, fa_mask_mode mask_mode, int batch, int n_q_
                      void* stream) {
   if (!lse) return FA_ERR_NULL_PTR;
   return run_fwd(dtype, mask_mode, batch, n_q_heads, n_kv_heads, seq_len, head_dim, scale, q, k,
-                 v, mask, nullptr, o, lse, stream);
+                 v, mask, nullptr, 1, o, lse, stream);
 }
 
 fa_status fa_fwd_ex(fa_dtype dtype, fa_mask_mode mask_mode, int batch, int n_q_heads,
                     int n_kv_heads, int seq_len, int head_dim, float scale, const void* q,
                     const void* k, const void* v, const uint32_t* mask, const uint32_t* tiles,
-                    void* o, float* lse, void* stream) {
+                    int kv_splits, void* o, float* lse, void* stream) {
   return run_fwd(dtype, mask_mode, batch, n_q_heads, n_kv_heads, seq_len, head_dim, scale, q, k,
-                 v, mask, tiles, o, lse, stream);
+                 v, mask, tiles, kv_splits, o, lse, stream);
 }
 
 }  // extern "C"

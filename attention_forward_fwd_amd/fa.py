@@ -51,7 +51,8 @@ def load() -> ctypes.CDLL:
         lib.fa_fwd_lse.restype = ctypes.c_int
         lib.fa_fwd_lse.argtypes = lib.fa_fwd.argtypes[:13] + [ctypes.c_void_p, ctypes.c_void_p]
         lib.fa_fwd_ex.restype = ctypes.c_int
-        lib.fa_fwd_ex.argtypes = lib.fa_fwd.argtypes[:12] + [ctypes.c_void_p] * 4
+        lib.fa_fwd_ex.argtypes = (lib.fa_fwd.argtypes[:12] + [ctypes.c_void_p, ctypes.c_int]
+                                  + [ctypes.c_void_p] * 3)
         for name in ("fa_pack_mask", "fa_mask_tiles"):
             f = getattr(lib, name)
             f.restype = ctypes.c_int
@@ -87,10 +88,10 @@ def fa_fwd_lse_raw(dtype: int, mask_mode: int, batch: int, n_q_heads: int, n_kv_
 
 def fa_fwd_ex_raw(dtype: int, mask_mode: int, batch: int, n_q_heads: int, n_kv_heads: int,
                   seq_len: int, head_dim: int, scale: float, q: int, k: int, v: int, mask: int,
-                  tiles: int, o: int, lse: int, stream: int) -> int:
+                  tiles: int, kv_splits: int, o: int, lse: int, stream: int) -> int:
     """Direct call of fa_fwd_ex with integer pointers (0 = NULL); returns the fa_status code."""
     return load().fa_fwd_ex(dtype, mask_mode, batch, n_q_heads, n_kv_heads, seq_len, head_dim,
-                            ctypes.c_float(scale), q, k, v, mask, tiles, o, lse, stream)
+                            ctypes.c_float(scale), q, k, v, mask, tiles, kv_splits, o, lse, stream)
 
 
 def _tiles_ptr(tiles, mode, B, Hq, S):
@@ -144,20 +145,23 @@ def _args(q, k, v, mode, scale, mask, out):
 
 def fa_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, mode: str = "none",
            scale: float | None = None, mask: torch.Tensor | None = None,
-           out: torch.Tensor | None = None, tiles: torch.Tensor | None = None) -> torch.Tensor:
+           out: torch.Tensor | None = None, tiles: torch.Tensor | None = None,
+           kv_splits: int = 1) -> torch.Tensor:
     """O = softmax(scale Q K^T + mask) V on the GPU (see include/fa.h for the definition).
 
     q [B,S,Hq,D], k/v [B,S,Hkv,D] (bf16 or fp16, contiguous, on one GPU); mask [B,Hq,S,ceil(S/32)]
     int32/uint32 words for mode "bitmask"; tiles (optional, bitmask mode) the mask's per-block
-    summary from mask_tiles, so dead 64-key tiles are not loaded.  Enqueued on torch's current
+    summary from mask_tiles, so dead 64-key tiles are not loaded; kv_splits: 1 = no split-KV,
+    0 = automatic, 2..16 = that many key ranges per row tile.  Enqueued on torch's current
     stream; returns o."""
     B, S, Hq, Hkv, D, scale, mptr, out = _args(q, k, v, mode, scale, mask, out)
     tptr = _tiles_ptr(tiles, mode, B, Hq, S)
     stream = torch.cuda.current_stream(q.device).cuda_stream
     with torch.cuda.device(q.device):
-        if tptr:
+        if tptr or kv_splits != 1:
             st = fa_fwd_ex_raw(DTYPES[q.dtype], MODES[mode], B, Hq, Hkv, S, D, scale, q.data_ptr(),
-                               k.data_ptr(), v.data_ptr(), mptr, tptr, out.data_ptr(), 0, stream)
+                               k.data_ptr(), v.data_ptr(), mptr, tptr, int(kv_splits),
+                               out.data_ptr(), 0, stream)
         else:
             st = fa_fwd_raw(DTYPES[q.dtype], MODES[mode], B, Hq, Hkv, S, D, scale, q.data_ptr(),
                             k.data_ptr(), v.data_ptr(), mptr, out.data_ptr(), stream)
@@ -169,7 +173,7 @@ def fa_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, mode: str = "none"
 def fa_fwd_lse(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, mode: str = "none",
                scale: float | None = None, mask: torch.Tensor | None = None,
                out: torch.Tensor | None = None, lse: torch.Tensor | None = None,
-               tiles: torch.Tensor | None = None):
+               tiles: torch.Tensor | None = None, kv_splits: int = 1):
     """As fa_fwd, also returning the log-sum-exp of each row's kept scores.
 
     Returns (o, lse) with lse [B, Hq, S] float32 (-inf for a row with no kept key)."""
@@ -183,8 +187,8 @@ def fa_fwd_lse(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, mode: str = "n
     stream = torch.cuda.current_stream(q.device).cuda_stream
     with torch.cuda.device(q.device):
         st = fa_fwd_ex_raw(DTYPES[q.dtype], MODES[mode], B, Hq, Hkv, S, D, scale, q.data_ptr(),
-                           k.data_ptr(), v.data_ptr(), mptr, tptr, out.data_ptr(), lse.data_ptr(),
-                           stream)
+                           k.data_ptr(), v.data_ptr(), mptr, tptr, int(kv_splits),
+                           out.data_ptr(), lse.data_ptr(), stream)
     if st != 0:
         raise FaError(st, fa_status_string(st))
     return out, lse

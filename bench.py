@@ -8,8 +8,8 @@ https://yetianai.com/news/16520, section "七天跑出的成绩单").  The causa
 shape, every other workload of the grid (other sequence lengths, GQA, the short random-mask
 cases), the default workload through fa_fwd_lse (O plus the per-row log-sum-exp) and the mask
 kernels (byte-mask packing and the tile summary, on the B16 H16 S1000 shape) and a packed-document
-mask on that shape (dense walk vs the tile-summary walk) are timed alongside and reported under
-"also".
+mask on that shape (dense walk vs the tile-summary walk) and split-KV on small grids (one
+sequence with one or two heads) are timed alongside and reported under "also".
 
 Prints ONE JSON line.  FLOPs are counted dense, 4*B*Hq*S^2*d, half of that for causal.
 """
@@ -152,6 +152,28 @@ def time_document_mask(inputs, dev, steps):
     return out
 
 
+def time_split_kv(inputs, dev, steps):
+    """Split-KV on small grids (one sequence, one or two heads, so few workgroups): the call
+    without splitting against the automatic split (kv_splits=0)."""
+    import torch
+    from attention_forward_fwd_amd import fa_fwd
+    out = {}
+    for H, S, causal in ((1, 32768, False), (1, 32768, True), (2, 16384, False), (1, 4096, False)):
+        w = inputs.Workload("small-grid", "bf16", "causal" if causal else "none", 1, S, H, H, 128,
+                            seed=6000 + H * 10 + (1 if causal else 0))
+        q, k, v = inputs.make_qkv_device(w, dev)
+        o = torch.empty_like(q)
+        f = flops(1, H, S, 128, w.mode)
+        rec = {}
+        for name, splits in (("no split", 1), ("auto split", 0)):
+            ms = time_launches(lambda: fa_fwd(q, k, v, mode=w.mode, scale=w.scale, out=o,
+                                              kv_splits=splits), steps, 3)
+            rec[name] = {"ms": ms, "tflops": f / (ms * 1e-3) / 1e12}
+        out[w.label] = rec
+        del q, k, v, o
+    return out
+
+
 def cpu_baseline(w, q, k, v, mask, o_gpu, budget_s):
     """Time the fp64 oracle on a bounded sample of the same workload (row blocks of one head
     at full key length, as many as fit in budget_s) and check the GPU rows it covers."""
@@ -272,6 +294,7 @@ def main():
         del lse
         also.update(time_mask_kernels(inputs, dev, 50))
         also.update(time_document_mask(inputs, dev, 100))
+        also["split-kv"] = time_split_kv(inputs, dev, 10)
 
     bytes_alg = alg_bytes(w)   # Q, K, V (and mask) read + O written
     # HBM bytes per launch measured with rocprofv3 byte counters (profiles/traffic.json); only

@@ -58,7 +58,7 @@
 extern "C" {
 #endif
 
-#define FA_ABI_VERSION 4
+#define FA_ABI_VERSION 5
 
 typedef enum {
   FA_MASK_NONE = 0,     /* every key kept */
@@ -103,7 +103,7 @@ fa_status fa_fwd_lse(fa_dtype dtype, fa_mask_mode mask_mode, int batch, int n_q_
                      const void* k, const void* v, const uint32_t* mask, void* o, float* lse,
                      void* stream);
 
-/* The general form: fa_fwd plus two optional arguments.
+/* The general form: fa_fwd plus three optional arguments.
  *   lse    NULL, or as for fa_fwd_lse.
  *   tiles  NULL, or (FA_MASK_BITMASK only) the per-block summary of `mask` made by
  *          fa_mask_tiles below ([batch, n_q_heads, R, TW] uint32, R = ceil(seq_len / 64),
@@ -114,12 +114,23 @@ fa_status fa_fwd_lse(fa_dtype dtype, fa_mask_mode mask_mode, int batch, int n_q_
  *          every kept bit of `mask` (fa_mask_tiles' output, or any superset of its set bits):
  *          keys in tiles it marks empty are treated as masked.  With a valid summary the
  *          result equals fa_fwd's (bitwise).
+ *   kv_splits  split-KV: 1 = off (fa_fwd's schedule); N in 2..16 = each row tile's key range
+ *          is cut into N equal shares computed by separate workgroups, whose running states
+ *          (max, row sum, unnormalised O) are combined by a second kernel exactly as the
+ *          online softmax combines tiles; 0 = automatic: split (into up to 16 shares of at
+ *          least 8 key tiles) only when the grid would fill at most half of the chip.  This
+ *          keeps a small grid -- one long sequence with few heads -- from leaving CUs idle.
+ *          Splitting changes the summation order, so O and lse then agree with fa_fwd's to the
+ *          stated tolerances, not bitwise.  Not combined with tiles.  Workspace: n_splits x
+ *          batch x seq_len x n_q_heads x (head_dim + 2) x 4 bytes, stream-ordered from the
+ *          same pool as the packed-V buffer (see above); one more kernel is enqueued.
  * Errors as for fa_fwd, plus: tiles with another mask mode -> FA_ERR_BAD_MASK_MODE;
- * misaligned lse or tiles, or R > 2048, -> FA_ERR_UNSUPPORTED. */
+ * misaligned lse or tiles, R > 2048, kv_splits outside 0..16, or kv_splits > 1 with tiles
+ * -> FA_ERR_UNSUPPORTED. */
 fa_status fa_fwd_ex(fa_dtype dtype, fa_mask_mode mask_mode, int batch, int n_q_heads,
                     int n_kv_heads, int seq_len, int head_dim, float scale, const void* q,
                     const void* k, const void* v, const uint32_t* mask, const uint32_t* tiles,
-                    void* o, float* lse, void* stream);
+                    int kv_splits, void* o, float* lse, void* stream);
 
 /* Packs a byte mask into the layout fa_fwd reads in FA_MASK_BITMASK mode.
  *   mask_bytes [batch, n_heads, seq_len, seq_len] uint8, one byte per (query row, key):

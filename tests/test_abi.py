@@ -53,9 +53,9 @@ def test_no_vendor_math_library_linked():
 
 def test_abi_version_and_status_strings():
     lib = _lib()
-    assert lib.fa_abi_version() == 4
+    assert lib.fa_abi_version() == 5
     header = open(HEADER).read()
-    assert re.search(r"#define FA_ABI_VERSION 4\b", header)
+    assert re.search(r"#define FA_ABI_VERSION 5\b", header)
     for code, name in fab.STATUS.items():
         s = fa.fa_status_string(code)
         assert s and isinstance(s, str)
@@ -105,15 +105,16 @@ def test_lse_entry_invalid_arguments_rejected(kw, status):
     (dict(tiles=P), 4), (dict(mode=1, tiles=P), 4), (dict(mode=2, mask=P, tiles=P + 2), 3),
     (dict(mode=2, mask=P, tiles=P, S=131073, D=64, Hq=1), 3), (dict(mode=2, mask=P, lse=P + 1), 3),
     (dict(q=0), 1), (dict(mode=2, mask=0, tiles=P), 4),
+    (dict(splits=-1), 3), (dict(splits=17), 3), (dict(mode=2, mask=P, tiles=P, splits=2), 3),
 ])
 def test_ex_entry_validates(kw, status):
     _lib()
     a = dict(dtype=1, mode=0, B=1, Hq=2, Hkv=1, S=8, D=128, scale=0.1, q=P, k=P, v=P, mask=0,
-             tiles=0, o=P, lse=0)
+             tiles=0, splits=1, o=P, lse=0)
     a.update(kw)
     assert fa.fa_fwd_ex_raw(a["dtype"], a["mode"], a["B"], a["Hq"], a["Hkv"], a["S"], a["D"],
-                            a["scale"], a["q"], a["k"], a["v"], a["mask"], a["tiles"], a["o"],
-                            a["lse"], 0) == status
+                            a["scale"], a["q"], a["k"], a["v"], a["mask"], a["tiles"],
+                            a["splits"], a["o"], a["lse"], 0) == status
 
 
 @pytest.mark.parametrize("lse,status", [(0, 1), (P + 2, 3)])
