@@ -47,6 +47,10 @@
 //     diagonal, empty blocks of a custom mask).  Causal workgroups stop at their last live tile.
 //   * Scheduling: workgroups are remapped so each of the 8 XCDs gets a contiguous range of
 //     tiles (tiles of one KV head share that XCD's L2); causal row tiles run longest first.
+//   * Optional outputs and schedules (fa_fwd_ex): each row's log-sum-exp from the running
+//     softmax state; in bitmask mode a walk over only the key tiles a per-block mask summary
+//     marks live (no loads for the others); split-KV, where shares of a row tile's key range
+//     run in separate workgroups and merge_kernel combines their (max, sum, O) states.
 
 #include <hip/hip_runtime.h>
 #include <math.h>
@@ -669,8 +673,9 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void fa_fwd_kernel(Params
     else return *(const u32x4*)(vb + vt_base + ks * Vt<D>::KSS + db * Vt<D>::RGS);
   };
 
-  // ---- Tile pipeline.  Iteration j writes V_{j+1}^T to LDS (from registers loaded one iteration
-  // earlier) and issues the loads of the mask words of tile j+2 (registers), K_{j+2} (DMA into
+  // ---- Tile pipeline ("tile j" is the j-th tile of the walk: tix(j)).  Iteration j writes
+  // V_{j+1}^T to LDS (from registers loaded one iteration earlier, or by DMA from the packed
+  // tiles) and issues the loads of the mask words of tile j+2 (registers), K_{j+2} (DMA into
   // LDS) and V_{j+2} (registers), then runs two phases:
   //   1. S_{j+1} = K_{j+1} Q^T on the matrix cores while the vector units run the masked online
   //      softmax of S_j (computed one iteration earlier), in one instruction stream that the
@@ -680,8 +685,8 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void fa_fwd_kernel(Params
   // and ends at the one workgroup barrier of the tile.  K and V are loaded two tiles ahead (V
   // lands in registers and is transposed into LDS one iteration later, in phase 1, off the
   // barrier's path), the mask words one; the keep words of tile j are carried in registers
-  // from iteration j-1, so the mask buffer of tile j can be refilled during iteration j.  Loads past the last tile
-  // re-read the last tile (in bounds, never used).
+  // from iteration j-1, so the mask buffer of tile j can be refilled during iteration j.
+  // Loads past the last tile re-read the last tile (in bounds, never used).
 
   // S^T = K Q^T for one tile, each operand read QA matrix instructions ahead.
   constexpr int QA = FA_QK_AHEAD;

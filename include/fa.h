@@ -45,7 +45,8 @@
  *
  * Errors: arguments are validated first, synchronously, with no HIP call; on error nothing is
  * enqueued and o is untouched.  A failed workspace allocation or a launch error reported by
- * HIP returns FA_ERR_HIP (after an allocation failure nothing is enqueued).  Faults during
+ * HIP returns FA_ERR_HIP (after an allocation failure no kernel is enqueued; a buffer the call
+ * had already taken is returned to the pool stream-ordered).  Faults during
  * execution surface at the caller's next synchronisation, as for any HIP kernel.  Nothing is
  * printed and no C++ exception crosses this interface.
  */
