@@ -55,17 +55,27 @@ __global__ __launch_bounds__(256) void pack_rows_kernel(const uint8_t* __restric
   constexpr int PARTS = 32 / V;   // pieces per word
   constexpr int LOADS = 32 / V;   // load instructions per 2 KiB run (64 words)
   constexpr int IPW = kItemsPerWave;
-  const long long item0 = ((long long)blockIdx.x * 4 + (threadIdx.x >> 6)) * IPW;
+  // (wave-uniform indices: the row and run arithmetic stays on the scalar unit)
+  const long long item0 =
+      ((long long)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6)) * IPW;
   const int lane = threadIdx.x & 63;
   if (item0 >= n_items) return;  // (whole waves)
   u32 v[IPW];
+  long long rows_[IPW];
+  int segs[IPW];
+#pragma unroll
+  for (int it = 0; it < IPW; ++it) {
+    const long long item = item0 + it;
+    rows_[it] = n_seg == 1 ? item : item / n_seg;
+    segs[it] = (int)(item - rows_[it] * n_seg);
+  }
 #pragma unroll
   for (int it = 0; it < IPW; ++it) {
     v[it] = 0u;
     const long long item = item0 + it;
     if (item < n_items) {
-      const long long row = item / n_seg;
-      const int seg = (int)(item - row * n_seg);
+      const long long row = rows_[it];
+      const int seg = segs[it];
       const uint8_t* rb = bytes + row * (long long)S;
 #pragma unroll
       for (int e = 0; e < LOADS; ++e) {
@@ -93,9 +103,8 @@ __global__ __launch_bounds__(256) void pack_rows_kernel(const uint8_t* __restric
       w |= ((__shfl((int)v[it], src + k) >> (V * e)) & ((1u << V) - 1u)) << (V * k);
     const long long item = item0 + it;
     if (item < n_items) {
-      const long long row = item / n_seg;
-      const int wi = 64 * (int)(item - row * n_seg) + j;
-      if (wi < W) words[row * W + wi] = w;
+      const int wi = 64 * segs[it] + j;
+      if (wi < W) words[rows_[it] * W + wi] = w;
     }
   }
 }
@@ -148,7 +157,7 @@ __global__ __launch_bounds__(256) void pack_kernel(const uint8_t* __restrict__ b
 __global__ __launch_bounds__(256) void tiles_kernel(const u32* __restrict__ words,
                                                     u32* __restrict__ tiles, int S, int W,
                                                     int n_rb, int TW, long long n_waves) {
-  const long long wv = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const long long wv = (long long)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (wv >= n_waves) return;  // (whole waves)
   const long long rbh = wv / TW;
