@@ -2,7 +2,8 @@
 (mask_tiles), the result must equal the dense walk's bit for bit (O and LSE) and the oracle
 within the bitmask bounds, on structured masks (packed documents, cleared 64x64 blocks, a
 single live block, nothing kept), on each workgroup shape (128 rows, 256 rows, GQA groups,
-two summary words per block), and with a superset summary (every bit set)."""
+two summary words per block), with a superset summary (every bit set), and with an automatic
+split-KV request (which a tile walk never splits)."""
 
 import numpy as np
 import pytest
@@ -80,3 +81,15 @@ def test_sparse_superset_summary():
     tiles = torch.full((2, 4, R, (R + 31) // 32), -1, dtype=torch.int32, device=DEV)
     o_d, l_d, o_s, l_s, _ = _both(q, k, v, m, tiles)
     assert torch.equal(o_s, o_d) and torch.equal(l_s, l_d)
+
+
+def test_sparse_walk_with_automatic_split_request():
+    # kv_splits=0 (automatic) never splits a tile-summary walk: same result as the walk alone
+    w, q, k, v, m = _case(1000, 2, 2, 64, "f16", seed=13400)
+    m = inputs.document_mask(m, 3, seed=13401)
+    tiles = mask_tiles(m.to(DEV))
+    qd, kd, vd, md = q.to(DEV), k.to(DEV), v.to(DEV), m.to(DEV)
+    a = fa_fwd(qd, kd, vd, mode="bitmask", mask=md, tiles=tiles)
+    b = fa_fwd(qd, kd, vd, mode="bitmask", mask=md, tiles=tiles, kv_splits=0)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
