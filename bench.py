@@ -213,7 +213,7 @@ def cpu_baseline(w, q, k, v, mask, o_gpu, budget_s):
     }
 
 
-WORKLOADS = ("mha", "gqa4", "gqa8", "short-masked", "tiny-masked")
+WORKLOADS = ("mha", "gqa4", "gqa8", "short-masked", "document-masked", "tiny-masked")
 
 
 def pick_workload(inputs, name, batch, seq_len, causal):
@@ -223,6 +223,8 @@ def pick_workload(inputs, name, batch, seq_len, causal):
         return inputs.gqa_prefill(batch, seq_len, 4 if name == "gqa4" else 8, causal)
     if name == "short-masked":
         return inputs.short_masked(seq_len)
+    if name == "document-masked":
+        return inputs.document_masked(seq_len)
     return inputs.tiny_masked()
 
 
@@ -234,11 +236,15 @@ def main():
     ap.add_argument("--workload", choices=WORKLOADS, default="mha",
                     help="timed workload: MHA or GQA prefill (bf16, d128; --batch, --seq-len, "
                          "--causal), the short random-mask case (fp16, d64, B16 H16; --seq-len 512 "
-                         "or 1000) or the tiny masked case")
+                         "or 1000), the same shape with the mask confined to 4 packed documents per "
+                         "sequence (--seq-len, default 1000; --tile-walk), or the tiny masked case")
     ap.add_argument("--batch", type=int, default=4)
     ap.add_argument("--seq-len", type=int, default=None,
                     help="default 8192 for prefill, 512 for short-masked")
     ap.add_argument("--causal", action="store_true")
+    ap.add_argument("--tile-walk", action="store_true",
+                    help="masked workloads: pass the mask's tile summary, so each workgroup walks only "
+                         "the key tiles it keeps a key in")
     ap.add_argument("--cpu-budget", type=float, default=12.0,
                     help="seconds of oracle work for the CPU baseline (0 = skip)")
     ap.add_argument("--no-also", action="store_true",
@@ -257,11 +263,13 @@ def main():
     from attention_forward_fwd_amd import fa_fwd, fa_fwd_lse, inputs
 
     dev = torch.device("cuda:0")
-    seq_len = args.seq_len or (512 if args.workload == "short-masked" else 8192)
+    seq_len = args.seq_len or {"short-masked": 512, "document-masked": 1000}.get(args.workload, 8192)
     w = pick_workload(inputs, args.workload, args.batch, seq_len, args.causal)
     q, k, v = inputs.make_qkv(w)
     qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
     mask = inputs.make_bitmask(w) if w.mode == "bitmask" else None
+    if args.workload == "document-masked":
+        mask = inputs.document_mask(mask, w.extra["n_docs"], seed=w.seed + 1)
     maskd = mask.to(dev) if mask is not None else None
     out = torch.empty_like(qd)
 
@@ -274,8 +282,16 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
+    tiles = None
+    if args.tile_walk:
+        if w.mode != "bitmask":
+            print("--tile-walk applies to the masked workloads only", file=sys.stderr)
+            sys.exit(2)
+        from attention_forward_fwd_amd import mask_tiles
+        tiles = mask_tiles(maskd)
+
     def step():
-        fa_fwd(qd, kd, vd, mode=w.mode, scale=w.scale, mask=maskd, out=out)
+        fa_fwd(qd, kd, vd, mode=w.mode, scale=w.scale, mask=maskd, out=out, tiles=tiles)
 
     ms = time_launches(step, args.steps, args.warmup)
     f = flops(w.batch, w.n_q_heads, w.seq_len, w.head_dim, w.mode)
@@ -321,7 +337,8 @@ def main():
                 "frac": tflops / PEAK_BF16_TFLOPS, "traffic": traffic,
                 "algorithmic_bytes": bytes_alg, "kernel": kname}
     desc = {"mha": "MHA prefill", "gqa4": "GQA prefill", "gqa8": "GQA prefill",
-            "short-masked": "short random-mask", "tiny-masked": "tiny random-mask"}[args.workload]
+            "short-masked": "short random-mask", "document-masked": "packed-document mask",
+            "tiny-masked": "tiny random-mask"}[args.workload]
     mode_desc = {"none": "non-causal", "causal": "causal", "bitmask": "bitmask"}[w.mode]
     rec = {
         "metric": METRIC,
