@@ -87,3 +87,16 @@ def test_split_nothing_kept():
     m = torch.zeros_like(m)
     o, lse = _run(q, k, v, "bitmask", w.scale, m, 4)
     assert (o == 0).all() and np.isneginf(lse).all()
+
+
+@pytest.mark.parametrize("S,splits", [(65, 2), (65, 16), (130, 3), (200, 16)])
+@pytest.mark.parametrize("mode", ["none", "causal", "bitmask"])
+def test_split_short_ranges(S, splits, mode):
+    # shares capped at the tile count, shares of one tile, causal shares that are empty
+    w, q, k, v, m = _case(2, S, 3, 1, 64, "f16", mode, seed=14500 + S * 3 + splits)
+    label = f"split {splits} short S={S} {mode}"
+    log(f"case {label}")
+    o, lse = _run(q, k, v, mode, w.scale, m, splits)
+    want_o, want_lse = oracle.attention_lse(q, k, v, mode, w.scale, m)
+    compare(to64(o), want_o, q.dtype, label)
+    compare_lse(lse, want_lse, q.dtype, label)
