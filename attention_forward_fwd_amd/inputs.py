@@ -131,6 +131,28 @@ def document_mask(mask: torch.Tensor, n_docs: int, seed: int) -> torch.Tensor:
     return m
 
 
+def band_mask(mask: torch.Tensor, half_width: int) -> torch.Tensor:
+    """Copy of `mask` (any device) keeping only keys j with |j - i| <= half_width for query row
+    i (a sliding window); the random bits inside the band are kept as drawn."""
+    B, H, S, W = mask.shape
+    i = torch.arange(S, device=mask.device, dtype=torch.int64)[:, None]
+    key0 = torch.arange(W, device=mask.device, dtype=torch.int64)[None, :] * 32
+    lo = (i - half_width - key0).clamp(0, 32)          # first kept bit of each word
+    hi = (i + half_width + 1 - key0).clamp(0, 32)      # one past the last kept bit
+    hi = torch.maximum(hi, lo)
+    keep = (torch.ones_like(hi) << hi) - (torch.ones_like(lo) << lo)
+    return mask & keep.to(torch.uint32).view(torch.int32)
+
+
+def make_bitmask_device(w: Workload, device):
+    """Random packed mask words like make_bitmask (keep probability 0.5, every bit a fair coin),
+    drawn directly on `device` for sizes where the CPU would be slow; values differ from
+    make_bitmask's."""
+    g = torch.Generator(device=device).manual_seed(w.seed * 1009 + 7)
+    shape = (w.batch, w.n_q_heads, w.seq_len, mask_words(w.seq_len))
+    return torch.randint(-2 ** 31, 2 ** 31, shape, generator=g, device=device, dtype=torch.int64).to(torch.int32)
+
+
 # The benchmark grid.  Seed = 1000 * config + variant.
 def tiny_masked() -> Workload:
     return Workload("tiny-masked", "f16", "bitmask", 1, 128, 1, 1, 64, seed=1000)
