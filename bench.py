@@ -8,8 +8,9 @@ https://yetianai.com/news/16520, section "七天跑出的成绩单").  The causa
 shape, every other workload of the grid (other sequence lengths, GQA, the short random-mask
 cases), the default workload through fa_fwd_lse (O plus the per-row log-sum-exp) and the mask
 kernels (byte-mask packing and the tile summary, on the B16 H16 S1000 shape) and a packed-document
-mask on that shape (dense walk vs the tile-summary walk) and split-KV on small grids (one
-sequence with one or two heads) are timed alongside and reported under "also".
+mask on that shape and a sliding-window mask at S32768 (dense walk vs the tile-summary walk), and
+split-KV on small grids (one sequence with one or two heads) are timed alongside and reported
+under "also".
 
 Prints ONE JSON line.  FLOPs are counted dense, 4*B*Hq*S^2*d, half of that for causal.
 """
@@ -150,6 +151,28 @@ def time_document_mask(inputs, dev, steps):
         rec["live_tile_fraction"] = bits / (w.batch * w.n_q_heads * R * R)
     del q, k, v, m, tiles, o
     return out
+
+
+def time_sliding_window(inputs, dev, steps):
+    """A sliding-window mask (keys within 1024 positions of the query, random bits inside) at
+    B1 H16 S32768 fp16 d64: the dense walk against the walk over the tiles its summary marks live."""
+    import torch
+    from attention_forward_fwd_amd import fa_fwd, mask_tiles
+    w = inputs.Workload("sliding-window", "f16", "bitmask", 1, 32768, 16, 16, 64, seed=2200)
+    q, k, v = inputs.make_qkv_device(w, dev)
+    m = inputs.band_mask(inputs.make_bitmask_device(w, dev), 1024)
+    tiles = mask_tiles(m)
+    o = torch.empty_like(q)
+    f = flops(w.batch, w.n_q_heads, w.seq_len, w.head_dim, w.mode)
+    R = (w.seq_len + 63) // 64
+    live = int(sum(bin(int(x)).count("1") for x in tiles.cpu().numpy().view("uint32").ravel()))
+    rec = {"live_tile_fraction": live / (w.n_q_heads * R * R)}
+    for name, kw in (("dense walk", {}), ("tile walk", {"tiles": tiles})):
+        ms = time_launches(lambda: fa_fwd(q, k, v, mode="bitmask", scale=w.scale, mask=m, out=o, **kw),
+                           steps, 3)
+        rec[name] = {"ms": ms, "dense_equivalent_tflops": f / (ms * 1e-3) / 1e12}
+    del q, k, v, m, tiles, o
+    return {w.label: rec}
 
 
 def time_split_kv(inputs, dev, steps):
@@ -311,6 +334,7 @@ def main():
         also.update(time_mask_kernels(inputs, dev, 50))
         also.update(time_document_mask(inputs, dev, 100))
         also["split-kv"] = time_split_kv(inputs, dev, 10)
+        also.update(time_sliding_window(inputs, dev, 10))
 
     bytes_alg = alg_bytes(w)   # Q, K, V (and mask) read + O written
     # HBM bytes per launch measured with rocprofv3 byte counters (profiles/traffic.json); only
