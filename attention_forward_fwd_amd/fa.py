@@ -32,6 +32,28 @@ class FaError(RuntimeError):
         self.status = status
 
 
+class _OnDevice:
+    """Makes `index` the current HIP device for the call when it is not already (the library
+    launches on the current device); yields torch's current stream handle on that device."""
+    __slots__ = ("index", "prev")
+
+    def __init__(self, device):
+        self.index = device.index if device.index is not None else torch.cuda.current_device()
+        self.prev = None
+
+    def __enter__(self):
+        cur = torch.cuda.current_device()
+        if cur != self.index:
+            self.prev = cur
+            torch.cuda.set_device(self.index)
+        return torch.cuda.current_stream(self.index).cuda_stream
+
+    def __exit__(self, *exc):
+        if self.prev is not None:
+            torch.cuda.set_device(self.prev)
+        return False
+
+
 def lib_path() -> str:
     return _LIB_PATH
 
@@ -156,8 +178,7 @@ def fa_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, mode: str = "none"
     stream; returns o."""
     B, S, Hq, Hkv, D, scale, mptr, out = _args(q, k, v, mode, scale, mask, out)
     tptr = _tiles_ptr(tiles, mode, B, Hq, S)
-    stream = torch.cuda.current_stream(q.device).cuda_stream
-    with torch.cuda.device(q.device):
+    with _OnDevice(q.device) as stream:
         if tptr or kv_splits != 1:
             st = fa_fwd_ex_raw(DTYPES[q.dtype], MODES[mode], B, Hq, Hkv, S, D, scale, q.data_ptr(),
                                k.data_ptr(), v.data_ptr(), mptr, tptr, int(kv_splits),
@@ -184,8 +205,7 @@ def fa_fwd_lse(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, mode: str = "n
     elif (tuple(lse.shape) != (B, Hq, S) or lse.dtype != torch.float32 or not lse.is_contiguous()
           or lse.device != q.device):
         raise ValueError(f"lse must be a contiguous float32 tensor of shape {(B, Hq, S)} on q's device")
-    stream = torch.cuda.current_stream(q.device).cuda_stream
-    with torch.cuda.device(q.device):
+    with _OnDevice(q.device) as stream:
         st = fa_fwd_ex_raw(DTYPES[q.dtype], MODES[mode], B, Hq, Hkv, S, D, scale, q.data_ptr(),
                            k.data_ptr(), v.data_ptr(), mptr, tptr, int(kv_splits),
                            out.data_ptr(), lse.data_ptr(), stream)
@@ -219,8 +239,7 @@ def pack_mask(mask: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tens
         out = torch.empty((B, H, S, W), dtype=torch.int32, device=mask.device)
     elif tuple(out.shape) != (B, H, S, W) or out.dtype != torch.int32 or not out.is_contiguous():
         raise ValueError(f"out must be a contiguous int32 tensor of shape {(B, H, S, W)}")
-    stream = torch.cuda.current_stream(mask.device).cuda_stream
-    with torch.cuda.device(mask.device):
+    with _OnDevice(mask.device) as stream:
         st = fa_pack_mask_raw(B, H, S, mask.data_ptr(), out.data_ptr(), stream)
     if st != 0:
         raise FaError(st, fa_status_string(st))
@@ -243,8 +262,7 @@ def mask_tiles(words: torch.Tensor, out: torch.Tensor | None = None) -> torch.Te
         out = torch.empty((B, H, R, TW), dtype=torch.int32, device=words.device)
     elif tuple(out.shape) != (B, H, R, TW) or out.dtype != torch.int32 or not out.is_contiguous():
         raise ValueError(f"out must be a contiguous int32 tensor of shape {(B, H, R, TW)}")
-    stream = torch.cuda.current_stream(words.device).cuda_stream
-    with torch.cuda.device(words.device):
+    with _OnDevice(words.device) as stream:
         st = fa_mask_tiles_raw(B, H, S, words.data_ptr(), out.data_ptr(), stream)
     if st != 0:
         raise FaError(st, fa_status_string(st))
