@@ -109,8 +109,8 @@ struct Params {
 // rows: half the global->LDS traffic per FLOP), used when a KV head has many rows.
 constexpr int kBN = 64;           // keys per tile
 constexpr int kWide = 8;          // waves of the 256-row workgroup
-constexpr int kWideRows = 8192;   // rows per KV head (S x G) from which it is used
-constexpr int kWideRowsCausal = 8192;   // (causal: same threshold; measured +1.3 % at B4 S8192)
+constexpr int kWideRows = 4096;   // rows per KV head (S x G) from which it is used
+constexpr int kWideRowsCausal = 8192;   // (causal: its longer diagonal tail favours 128 rows below)
 constexpr int kPackRowTiles = 8;  // row tiles per KV head from which V is packed once up front
 constexpr int kMaxListTiles = 2048;  // key tiles a workgroup can list from a tile summary
 constexpr int kMaxSplits = 16;       // key ranges per row tile (split-KV)
