@@ -1095,15 +1095,23 @@ const char* fa_status_string(int s) {
 
 namespace {
 
-// fa_fwd, fa_fwd_lse and fa_fwd_ex: validation first (no HIP call), then the launches.
-fa_status run_fwd(fa_dtype dtype, fa_mask_mode mask_mode, int batch, int n_q_heads,
-                  int n_kv_heads, int seq_len, int head_dim, float scale, const void* q,
-                  const void* k, const void* v, const uint32_t* mask, const uint32_t* tiles,
-                  int kv_splits, void* o, float* lse, void* stream) {
+// The launch plan of a call: workgroup shape, V packing, split-KV shares and workspace, from the
+// sizes alone (shared by fa_fwd_plan and the launches, so the two always agree).
+struct Plan {
+  int nw;             // waves per workgroup (4: 128 rows, 8: 256 rows)
+  bool vpack;         // V^T packed by a pre-pass
+  int n_split;        // split-KV shares per row tile
+  int n_kt, n_rb, G;  // 64-key tiles, 64-row blocks, query heads per KV head
+  int64_t n_rt, n_wg; // row tiles per (batch, KV head); workgroups before splitting
+  size_t vt_bytes, part_bytes;  // packed V^T workspace, split-KV partials
+};
+
+fa_status make_plan(fa_dtype dtype, fa_mask_mode mask_mode, int batch, int n_q_heads,
+                    int n_kv_heads, int seq_len, int head_dim, bool with_tiles, int kv_splits,
+                    Plan* pl) {
   if (dtype != FA_DTYPE_F16 && dtype != FA_DTYPE_BF16) return FA_ERR_UNSUPPORTED;
   if (mask_mode != FA_MASK_NONE && mask_mode != FA_MASK_CAUSAL && mask_mode != FA_MASK_BITMASK)
     return FA_ERR_BAD_MASK_MODE;
-  if (!q || !k || !v || !o) return FA_ERR_NULL_PTR;
   if (batch <= 0 || n_q_heads <= 0 || n_kv_heads <= 0 || seq_len <= 0 ||
       n_q_heads % n_kv_heads != 0)
     return FA_ERR_BAD_SHAPE;
@@ -1121,27 +1129,62 @@ fa_status run_fwd(fa_dtype dtype, fa_mask_mode mask_mode, int batch, int n_q_hea
   const int64_t n_rt = (rows + nw * 32 - 1) / (nw * 32);
   const int64_t n_wg = n_rt * n_kv_heads * batch;
   if (n_wg >= ((int64_t)1 << 31)) return FA_ERR_BAD_SHAPE;
-  if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o) & 15u) return FA_ERR_UNSUPPORTED;
-  if (mask_mode == FA_MASK_BITMASK && (!mask || ((uintptr_t)mask & 3u))) return FA_ERR_BAD_MASK_MODE;
-  if (!isfinite(scale)) return FA_ERR_BAD_SCALE;
-  if (lse && ((uintptr_t)lse & 3u)) return FA_ERR_UNSUPPORTED;
   const int n_rb = (seq_len + 63) / 64;
-  if (tiles) {
+  if (with_tiles) {
     if (mask_mode != FA_MASK_BITMASK) return FA_ERR_BAD_MASK_MODE;
-    if (((uintptr_t)tiles & 3u) || n_rb > kMaxListTiles) return FA_ERR_UNSUPPORTED;
+    if (n_rb > kMaxListTiles) return FA_ERR_UNSUPPORTED;
   }
-  if (kv_splits < 0 || kv_splits > kMaxSplits || (tiles && kv_splits > 1)) return FA_ERR_UNSUPPORTED;
+  if (kv_splits < 0 || kv_splits > kMaxSplits || (with_tiles && kv_splits > 1))
+    return FA_ERR_UNSUPPORTED;
   // Split-KV: explicit, or (kv_splits == 0, no tile summary) when the grid fills at most half
   // of the chip's workgroup slots (one 256-row or two 128-row workgroups per CU): enough key
   // ranges per row tile to fill it, each at least 8 tiles long.
   int n_split = kv_splits > 1 ? min(kv_splits, n_kt) : 1;
-  if (kv_splits == 0 && !tiles) {
+  if (kv_splits == 0 && !with_tiles) {
     const int64_t slots = nw == kWide ? kNumCUs : 2 * kNumCUs;
     if (2 * n_wg <= slots)
       n_split = (int)std::min<int64_t>({(int64_t)kMaxSplits, (slots + n_wg - 1) / n_wg,
                                         std::max<int64_t>(1, n_kt / 8)});
   }
   if (n_wg * n_split >= ((int64_t)1 << 31)) return FA_ERR_BAD_SHAPE;
+  // Packed V^T (one pre-pass over V) when each KV head's V tiles would otherwise be transposed
+  // by kPackRowTiles or more row-tile workgroups (always so for the 256-row workgroup).
+  pl->nw = nw;
+  pl->vpack = pack_ok && (nw == kWide || n_rt >= kPackRowTiles);
+  pl->n_split = n_split;
+  pl->n_kt = n_kt;
+  pl->n_rb = n_rb;
+  pl->G = G;
+  pl->n_rt = n_rt;
+  pl->n_wg = n_wg;
+  pl->vt_bytes = pl->vpack ? (size_t)batch * n_kv_heads * n_kt * tile_bytes : 0;
+  pl->part_bytes = n_split > 1 ? (size_t)n_split * batch * seq_len * n_q_heads * (head_dim + 2) * 4 : 0;
+  return FA_OK;
+}
+
+// fa_fwd, fa_fwd_lse and fa_fwd_ex: validation first (no HIP call), then the launches.
+fa_status run_fwd(fa_dtype dtype, fa_mask_mode mask_mode, int batch, int n_q_heads,
+                  int n_kv_heads, int seq_len, int head_dim, float scale, const void* q,
+                  const void* k, const void* v, const uint32_t* mask, const uint32_t* tiles,
+                  int kv_splits, void* o, float* lse, void* stream) {
+  if (!q || !k || !v || !o) {
+    // (an unknown dtype or mode is reported first, as the plan would)
+    if (dtype != FA_DTYPE_F16 && dtype != FA_DTYPE_BF16) return FA_ERR_UNSUPPORTED;
+    if (mask_mode != FA_MASK_NONE && mask_mode != FA_MASK_CAUSAL && mask_mode != FA_MASK_BITMASK)
+      return FA_ERR_BAD_MASK_MODE;
+    return FA_ERR_NULL_PTR;
+  }
+  Plan pl;
+  const fa_status ps = make_plan(dtype, mask_mode, batch, n_q_heads, n_kv_heads, seq_len,
+                                 head_dim, tiles != nullptr, kv_splits, &pl);
+  if (ps != FA_OK) return ps;
+  if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o) & 15u) return FA_ERR_UNSUPPORTED;
+  if (mask_mode == FA_MASK_BITMASK && (!mask || ((uintptr_t)mask & 3u))) return FA_ERR_BAD_MASK_MODE;
+  if (!isfinite(scale)) return FA_ERR_BAD_SCALE;
+  if (lse && ((uintptr_t)lse & 3u)) return FA_ERR_UNSUPPORTED;
+  if (tiles && ((uintptr_t)tiles & 3u)) return FA_ERR_UNSUPPORTED;
+  const int nw = pl.nw, n_split = pl.n_split, n_kt = pl.n_kt, n_rb = pl.n_rb, G = pl.G;
+  const int64_t n_rt = pl.n_rt, n_wg = pl.n_wg;
 
   Params p;
   p.q = (const uint16_t*)q;
@@ -1179,9 +1222,7 @@ fa_status run_fwd(fa_dtype dtype, fa_mask_mode mask_mode, int batch, int n_q_hea
   p.qflip = scale < 0.f ? 0x80008000u : 0u;
 
   hipStream_t s = (hipStream_t)stream;
-  // Packed V^T (one pre-pass over V) when each KV head's V tiles would otherwise be transposed
-  // by kPackRowTiles or more row-tile workgroups (always so for the 256-row workgroup).
-  const bool vpack = pack_ok && (nw == kWide || n_rt >= kPackRowTiles);
+  const bool vpack = pl.vpack;
   hipError_t e = hipSuccess;
   void* ws = nullptr;    // packed V^T
   void* part = nullptr;  // split-KV partials
@@ -1191,14 +1232,14 @@ fa_status run_fwd(fa_dtype dtype, fa_mask_mode mask_mode, int batch, int n_q_hea
     if (e != hipSuccess) return FA_ERR_HIP;
   }
   if (n_split > 1) {
-    e = hipMallocFromPoolAsync(&part, (size_t)n_split * p.part_rows * (head_dim + 2) * 4, pool, s);
+    e = hipMallocFromPoolAsync(&part, pl.part_bytes, pool, s);
     if (e != hipSuccess) return FA_ERR_HIP;
     p.o_part = (float*)part;
     p.ml_part = p.o_part + (size_t)n_split * p.part_rows * head_dim;
     p.lse = nullptr;  // (written by the merge)
   }
   if (vpack) {
-    e = hipMallocFromPoolAsync(&ws, (size_t)batch * n_kv_heads * p.n_kt * tile_bytes, pool, s);
+    e = hipMallocFromPoolAsync(&ws, pl.vt_bytes, pool, s);
     if (e == hipSuccess) {
       p.vt = (const uint16_t*)ws;
       e = head_dim == 128 ? launch_pack<128>(p, batch, s) : launch_pack<64>(p, batch, s);
@@ -1246,6 +1287,23 @@ fa_status fa_fwd_lse(fa_dtype dtype, fa_mask_mode mask_mode, int batch, int n_q_
   if (!lse) return FA_ERR_NULL_PTR;
   return run_fwd(dtype, mask_mode, batch, n_q_heads, n_kv_heads, seq_len, head_dim, scale, q, k,
                  v, mask, nullptr, 1, o, lse, stream);
+}
+
+fa_status fa_fwd_plan(fa_dtype dtype, fa_mask_mode mask_mode, int batch, int n_q_heads,
+                      int n_kv_heads, int seq_len, int head_dim, int with_tiles, int kv_splits,
+                      fa_plan* plan) {
+  if (!plan) return FA_ERR_NULL_PTR;
+  Plan pl;
+  const fa_status st = make_plan(dtype, mask_mode, batch, n_q_heads, n_kv_heads, seq_len,
+                                 head_dim, with_tiles != 0, kv_splits, &pl);
+  if (st != FA_OK) return st;
+  plan->rows_per_workgroup = pl.nw * 32;
+  plan->packed_v = pl.vpack ? 1 : 0;
+  plan->kv_splits = pl.n_split;
+  plan->workgroups = pl.n_wg * pl.n_split;
+  plan->workspace_bytes = (uint64_t)(pl.vt_bytes + pl.part_bytes);
+  plan->kernels = 1 + (pl.vpack ? 1 : 0) + (pl.n_split > 1 ? 1 : 0);
+  return FA_OK;
 }
 
 fa_status fa_fwd_ex(fa_dtype dtype, fa_mask_mode mask_mode, int batch, int n_q_heads,

@@ -20,10 +20,17 @@ MODES = {"none": FA_MASK_NONE, "causal": FA_MASK_CAUSAL, "bitmask": FA_MASK_BITM
 DTYPES = {torch.float16: FA_DTYPE_F16, torch.bfloat16: FA_DTYPE_BF16}
 STATUS = {0: "FA_OK", 1: "FA_ERR_NULL_PTR", 2: "FA_ERR_BAD_SHAPE", 3: "FA_ERR_UNSUPPORTED",
           4: "FA_ERR_BAD_MASK_MODE", 5: "FA_ERR_BAD_SCALE", 6: "FA_ERR_HIP"}
-EXPORTS = ("fa_fwd", "fa_fwd_lse", "fa_fwd_ex", "fa_pack_mask", "fa_mask_tiles", "fa_status_string",
-           "fa_abi_version")
+EXPORTS = ("fa_fwd", "fa_fwd_lse", "fa_fwd_ex", "fa_fwd_plan", "fa_pack_mask", "fa_mask_tiles",
+           "fa_status_string", "fa_abi_version")
 
 _lib = None
+
+
+class FaPlan(ctypes.Structure):
+    """fa_plan of include/fa.h."""
+    _fields_ = [("rows_per_workgroup", ctypes.c_int), ("packed_v", ctypes.c_int),
+                ("kv_splits", ctypes.c_int), ("kernels", ctypes.c_int),
+                ("workgroups", ctypes.c_int64), ("workspace_bytes", ctypes.c_uint64)]
 
 
 class FaError(RuntimeError):
@@ -80,6 +87,8 @@ def load() -> ctypes.CDLL:
             f.restype = ctypes.c_int
             f.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
                           ctypes.c_void_p, ctypes.c_void_p]
+        lib.fa_fwd_plan.restype = ctypes.c_int
+        lib.fa_fwd_plan.argtypes = [ctypes.c_int] * 9 + [ctypes.POINTER(FaPlan)]
         lib.fa_status_string.restype = ctypes.c_char_p
         lib.fa_status_string.argtypes = [ctypes.c_int]
         lib.fa_abi_version.restype = ctypes.c_int
@@ -267,3 +276,14 @@ def mask_tiles(words: torch.Tensor, out: torch.Tensor | None = None) -> torch.Te
     if st != 0:
         raise FaError(st, fa_status_string(st))
     return out
+
+
+def fa_fwd_plan(dtype: int, mask_mode: int, batch: int, n_q_heads: int, n_kv_heads: int,
+                seq_len: int, head_dim: int, with_tiles: bool = False, kv_splits: int = 1) -> dict:
+    """The launch plan of a call with these sizes (see include/fa.h); raises FaError on bad sizes."""
+    plan = FaPlan()
+    st = load().fa_fwd_plan(dtype, mask_mode, batch, n_q_heads, n_kv_heads, seq_len, head_dim,
+                            int(bool(with_tiles)), kv_splits, ctypes.byref(plan))
+    if st != 0:
+        raise FaError(st, fa_status_string(st))
+    return {name: getattr(plan, name) for name, _ in FaPlan._fields_}

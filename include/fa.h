@@ -59,7 +59,7 @@
 extern "C" {
 #endif
 
-#define FA_ABI_VERSION 5
+#define FA_ABI_VERSION 6
 
 typedef enum {
   FA_MASK_NONE = 0,     /* every key kept */
@@ -132,6 +132,25 @@ fa_status fa_fwd_ex(fa_dtype dtype, fa_mask_mode mask_mode, int batch, int n_q_h
                     int n_kv_heads, int seq_len, int head_dim, float scale, const void* q,
                     const void* k, const void* v, const uint32_t* mask, const uint32_t* tiles,
                     int kv_splits, void* o, float* lse, void* stream);
+
+/* The launch plan of a call, from its sizes alone (no pointer, no HIP call, no GPU needed): what
+ * fa_fwd_ex with these arguments (with_tiles != 0: a tile summary is passed) would enqueue and
+ * how much workspace it would take from the pool.  fa_fwd and fa_fwd_lse are kv_splits = 1,
+ * with_tiles = 0.  The launches use the same planning code, so plan and call always agree. */
+typedef struct {
+  int rows_per_workgroup;    /* 128 (4 waves, two workgroups per CU) or 256 (8 waves, one) */
+  int packed_v;              /* 1: a pre-pass packs V into transposed tiles first */
+  int kv_splits;             /* key-range shares per row tile (1 = no split-KV) */
+  int kernels;               /* kernels enqueued: attention, + V pre-pass, + split-KV merge */
+  int64_t workgroups;        /* grid of the attention kernel */
+  uint64_t workspace_bytes;  /* device scratch taken stream-ordered from the pool, 0 if none */
+} fa_plan;
+
+/* Errors as for fa_fwd_ex's size, mode and kv_splits arguments; plan == NULL ->
+ * FA_ERR_NULL_PTR. */
+fa_status fa_fwd_plan(fa_dtype dtype, fa_mask_mode mask_mode, int batch, int n_q_heads,
+                      int n_kv_heads, int seq_len, int head_dim, int with_tiles, int kv_splits,
+                      fa_plan* plan);
 
 /* Packs a byte mask into the layout fa_fwd reads in FA_MASK_BITMASK mode.
  *   mask_bytes [batch, n_heads, seq_len, seq_len] uint8, one byte per (query row, key):

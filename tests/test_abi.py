@@ -53,9 +53,9 @@ def test_no_vendor_math_library_linked():
 
 def test_abi_version_and_status_strings():
     lib = _lib()
-    assert lib.fa_abi_version() == 5
+    assert lib.fa_abi_version() == 6
     header = open(HEADER).read()
-    assert re.search(r"#define FA_ABI_VERSION 5\b", header)
+    assert re.search(r"#define FA_ABI_VERSION 6\b", header)
     for code, name in fab.STATUS.items():
         s = fa.fa_status_string(code)
         assert s and isinstance(s, str)
@@ -155,3 +155,67 @@ def test_kernel_launch_stubs_defined():
     undef = subprocess.run(["nm", "-D", "--undefined-only", fa.lib_path()], capture_output=True,
                            text=True, check=True).stdout
     assert "fa_fwd_kernel" not in undef, [l for l in undef.splitlines() if "fa_fwd_kernel" in l]
+
+
+# ---------------------------------------------------------------- launch plan (host logic, no GPU)
+NONE, CAUSAL, BITMASK, BF16, F16 = 0, 1, 2, 1, 0
+
+
+def _plan(**kw):
+    a = dict(dtype=BF16, mode=NONE, B=4, Hq=16, Hkv=16, S=8192, D=128, tiles=False, splits=1)
+    a.update(kw)
+    _lib()
+    return fa.fa_fwd_plan(a["dtype"], a["mode"], a["B"], a["Hq"], a["Hkv"], a["S"], a["D"],
+                          a["tiles"], a["splits"])
+
+
+def test_plan_prefill_uses_256_row_workgroups_and_packed_v():
+    p = _plan()
+    n_kt = 8192 // 64
+    assert p["rows_per_workgroup"] == 256 and p["packed_v"] == 1 and p["kv_splits"] == 1
+    assert p["workgroups"] == 4 * 16 * 8192 // 256 and p["kernels"] == 2
+    assert p["workspace_bytes"] == 4 * 16 * n_kt * 64 * 128 * 2      # packed V^T: about V's size
+
+
+def test_plan_row_thresholds():
+    # 256-row workgroups from 4096 rows per KV head (S x G), 8192 for causal
+    assert _plan(B=8, S=4096)["rows_per_workgroup"] == 256
+    assert _plan(B=8, S=4096, mode=CAUSAL)["rows_per_workgroup"] == 128
+    assert _plan(B=4, S=8192, mode=CAUSAL)["rows_per_workgroup"] == 256
+    assert _plan(B=16, S=2048)["rows_per_workgroup"] == 128
+    assert _plan(B=16, S=2048, Hq=32, Hkv=8)["rows_per_workgroup"] == 256   # 2048 x 4 rows
+
+
+def test_plan_short_masked():
+    # S = 512: four 128-row tiles per head, V transposed in-kernel, nothing allocated
+    p = _plan(dtype=F16, mode=BITMASK, B=16, S=512, D=64)
+    assert p == {"rows_per_workgroup": 128, "packed_v": 0, "kv_splits": 1, "kernels": 1,
+                 "workgroups": 16 * 16 * 4, "workspace_bytes": 0}
+    # S = 1000: eight row tiles per head -> V packed once per call (16 tiles x 8 KiB per head)
+    p = _plan(dtype=F16, mode=BITMASK, B=16, S=1000, D=64)
+    assert p["packed_v"] == 1 and p["workspace_bytes"] == 16 * 16 * 16 * 64 * 64 * 2
+
+
+def test_plan_split_kv():
+    # explicit shares are capped at the key tiles; the partials are n x B x S x Hq x (d + 2) x 4 B
+    p = _plan(B=1, Hq=1, Hkv=1, S=130, splits=16)
+    assert p["kv_splits"] == 3 and p["kernels"] == 2
+    assert p["workspace_bytes"] == 3 * 130 * (128 + 2) * 4
+    # automatic: a small grid (one head, S = 4096: 32 row tiles of 128 rows) is split to fill
+    # the chip, at least 8 key tiles per share
+    p = _plan(B=1, Hq=1, Hkv=1, S=4096, splits=0)
+    assert p["rows_per_workgroup"] == 256 and p["kv_splits"] == 8 and p["workgroups"] == 16 * 8
+    # automatic on a full grid, or with a tile summary: no split
+    assert _plan(splits=0)["kv_splits"] == 1
+    assert _plan(mode=BITMASK, B=1, Hq=1, Hkv=1, S=4096, tiles=True, splits=0)["kv_splits"] == 1
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dtype=9), 3), (dict(mode=5), 4), (dict(S=0), 2), (dict(Hq=6, Hkv=4), 2), (dict(D=96), 3),
+    (dict(tiles=True), 4), (dict(splits=17), 3), (dict(mode=BITMASK, tiles=True, splits=2), 3),
+    (dict(mode=BITMASK, tiles=True, S=131073, Hq=1, Hkv=1, D=64), 3),
+])
+def test_plan_rejects_what_the_call_rejects(kw, status):
+    with pytest.raises(fab.FaError) as ei:
+        _plan(**kw)
+    assert ei.value.status == status

@@ -48,7 +48,7 @@ def test_split_explicit(splits, mode, D, dtype):
 
 @pytest.mark.parametrize("mode", ["none", "causal"])
 def test_split_auto_small_grid(mode):
-    # one head, 4096 positions: 32 row tiles of 128 rows, a sixteenth of the chip's slots
+    # one head, 4096 positions: 16 row tiles of 256 rows, a sixteenth of the chip's slots
     w, q, k, v, _ = _case(1, 4096, 1, 1, 128, "bf16", mode, seed=14100)
     label = f"auto split {mode} B1 H1 S4096"
     log(f"case {label}")
