@@ -40,8 +40,11 @@
 //     writes).  Buffer resources end at the sequence: key rows past it read as zeros and are
 //     masked, so their probabilities are exactly 0.  Q is staged once through LDS into registers.
 //   * Softmax: exp2 with log2(e) folded into the scale, running max floored at -1e30 so a
-//     fully masked row never makes NaN, unconditional (branch-free) rescale of O and l every
-//     tile, masked scores set to -inf with one bit-field extract and one bit-field insert.
+//     fully masked row never makes NaN, masked scores set to -inf with one bit-field extract
+//     and one bit-field insert.  The running max is lazy: it moves only when a tile's max
+//     exceeds it by more than 8 (exp2 domain), so P stays below 2^8 and alpha is exactly 1 on
+//     almost every tile.  The rescale of O has no per-lane branch; a wave in which every lane
+//     has alpha == 1 skips it by one wave-uniform (scalar) branch.
 //   * Skips: per wave and tile, the keep bits of the wave's rows are voted with a 64-lane
 //     ballot; a tile with no kept bit costs no matrix or softmax work (causal tiles above the
 //     diagonal, empty blocks of a custom mask).  Causal workgroups stop at their last live tile.
@@ -115,6 +118,10 @@ constexpr int kPackRowTiles = 8;  // row tiles per KV head from which V is packe
 constexpr int kMaxListTiles = 2048;  // key tiles a workgroup can list from a tile summary
 constexpr int kMaxSplits = 16;       // key ranges per row tile (split-KV)
 constexpr int kNumCUs = 256;         // MI355X compute units (automatic split-KV sizing)
+// Lazy running max: a row's max (in the exp2 domain) moves only when a tile's max exceeds it by
+// more than kMaxSlack, so P = 2^(s c - m) stays below 2^kMaxSlack (exact in bf16/fp16 and far
+// from overflow in the fp32 sums), and a wave whose rows all keep their max skips the rescale.
+constexpr float kMaxSlack = 8.f;
 #ifndef FA_P1_VALU
 #define FA_P1_VALU 8
 #endif
@@ -740,7 +747,10 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void fa_fwd_kernel(Params
     }
     float mx = __builtin_fmaxf(__builtin_fmaxf(mx4[0], mx4[1]), __builtin_fmaxf(mx4[2], mx4[3]));
     mx = max_halves(mx);
-    const float m_new = fmaxf(m_run, mx * c);
+    // The max moves only past the slack (then straight to the tile's max); otherwise alpha is
+    // exactly 1.  A first live tile always moves it off the -1e30 floor; an all -inf tile never.
+    const float mt = mx * c;
+    const float m_new = mt > m_run + kMaxSlack ? mt : m_run;
     const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
     m_run = m_new;
     // p = 2^(s*c - m), rounded to the input dtype; the row sum adds the rounded values
@@ -762,8 +772,10 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void fa_fwd_kernel(Params
     return alpha;
   };
 
-  // O = alpha O + V^T P^T (branch-free rescale, P straight from registers), each V^T operand
-  // read PA matrix instructions ahead.
+  // O = alpha O + V^T P^T (P straight from registers), each V^T operand read PA matrix
+  // instructions ahead.  The rescale has no per-lane branch: a wave whose rows all kept their max
+  // (alpha == 1 in every lane, the common case under the lazy max) skips it as a whole, by one
+  // scalar branch on a 64-lane ballot; otherwise every lane multiplies.
   constexpr int PA = FA_PV_AHEAD;
   auto pv = [&](const unsigned char* vb, const u32x4 (&pk)[PKS], float alpha)
                 __attribute__((always_inline)) {
@@ -771,10 +783,12 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void fa_fwd_kernel(Params
     u32x4 va[PA + 1];
 #pragma unroll
     for (int i = 0; i < PA; ++i) va[i] = v_operand(vb, i % PKS, i / PKS);
+    if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {
 #pragma unroll
-    for (int db = 0; db < NDB; ++db)
+      for (int db = 0; db < NDB; ++db)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+        for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+    }
 #pragma unroll
     for (int i = 0; i < N; ++i) {
       if (i + PA < N) va[(i + PA) % (PA + 1)] = v_operand(vb, (i + PA) % PKS, (i + PA) / PKS);
