@@ -123,13 +123,13 @@ constexpr int kNumCUs = 256;         // MI355X compute units (automatic split-KV
 // from overflow in the fp32 sums), and a wave whose rows all keep their max skips the rescale.
 constexpr float kMaxSlack = 8.f;
 #ifndef FA_P1_VALU
-#define FA_P1_VALU 8
+#define FA_P1_VALU 4
 #endif
 #ifndef FA_QK_AHEAD
 #define FA_QK_AHEAD 3
 #endif
 #ifndef FA_PV_AHEAD
-#define FA_PV_AHEAD 3
+#define FA_PV_AHEAD 4
 #endif
 
 template <bool BF16>
