@@ -144,6 +144,15 @@ def band_mask(mask: torch.Tensor, half_width: int) -> torch.Tensor:
     return mask & keep.to(torch.uint32).view(torch.int32)
 
 
+def growing_keys(k: torch.Tensor, gain: float) -> torch.Tensor:
+    """Copy of K [B,S,H,D] with key row j multiplied by 1 + gain * j / S (then rounded back to
+    K's dtype): the scores' spread, and so each query's running maximum over the keys seen so
+    far, keeps growing along the sequence instead of settling after the first few keys."""
+    S = k.shape[1]
+    f = 1.0 + gain * torch.arange(S, dtype=torch.float32) / S
+    return (k.float() * f[None, :, None, None]).to(k.dtype)
+
+
 def make_bitmask_device(w: Workload, device):
     """Random packed mask words like make_bitmask (keep probability 0.5, every bit a fair coin),
     drawn directly on `device` for sizes where the CPU would be slow; values differ from

@@ -209,3 +209,29 @@ def test_no_out_of_bounds_writes(S):
     assert (buf[:pad] == 12345.0).all() and (buf[pad + n:] == 12345.0).all(), "guard band written"
     want = oracle.attention(q, k, v, "causal", D ** -0.5)
     compare(to64(out), want, q.dtype, f"guarded S={S}")
+
+
+# ----------------------------------------------------------------- a running max that keeps moving
+# Key rows scaled by 1 + 20 j / S: scaled scores (exp2 domain) reach a spread of ~30 near the
+# end, so each row's running maximum rises past the kernel's slack many times along the
+# sequence and the rescale of O and of the row sum runs repeatedly, on every workgroup shape.
+@pytest.mark.parametrize("mode,D,dtype,B,S,Hq,Hkv,full", [
+    ("none", 128, "bf16", 1, 4096, 2, 2, False),     # 256-row workgroups, packed V^T
+    ("causal", 128, "bf16", 1, 8192, 1, 1, False),   # 256-row causal workgroups
+    ("none", 128, "bf16", 1, 1024, 8, 2, True),      # GQA group of 4, 256-row workgroups
+    ("causal", 128, "bf16", 2, 700, 4, 4, True),     # 128-row workgroups, V^T in-kernel
+    ("bitmask", 64, "f16", 2, 1000, 2, 2, True),     # 128-row workgroups, packed V^T
+    ("bitmask", 128, "f16", 1, 300, 3, 1, True),     # GQA group of 3, ragged tail
+    ("none", 64, "f16", 1, 333, 2, 1, True),
+], ids=lambda x: str(x))
+def test_growing_max(mode, D, dtype, B, S, Hq, Hkv, full):
+    w = inputs.Workload("grow", dtype, mode, B, S, Hq, Hkv, D, seed=17000 + S + D)
+    q, k, v = inputs.make_qkv(w)
+    k = inputs.growing_keys(k, 20.0)
+    m = inputs.make_bitmask(w) if mode == "bitmask" else None
+    label = f"growing max {mode} d{D} {dtype} B{B} S{S} H{Hq}/{Hkv}"
+    log(f"case {label}")
+    if full:
+        check_full(q, k, v, mode, w.scale, m, label)
+    else:
+        check_sampled(q, k, v, mode, w.scale, m, label, seed=w.seed)

@@ -100,3 +100,19 @@ def test_split_short_ranges(S, splits, mode):
     want_o, want_lse = oracle.attention_lse(q, k, v, mode, w.scale, m)
     compare(to64(o), want_o, q.dtype, label)
     compare_lse(lse, want_lse, q.dtype, label)
+
+
+@pytest.mark.parametrize("splits", [1, 4])
+@pytest.mark.parametrize("mode", ["none", "causal", "bitmask"])
+def test_growing_max_split_lse(mode, splits):
+    # Key rows scaled by 1 + 20 j / S: each row's running maximum keeps rising past the kernel's
+    # slack, so every share ends on its own (lagging) maximum and the merge and the LSE must still
+    # reproduce the oracle.
+    w, q, k, v, m = _case(1, 1100, 4, 2, 128, "bf16", mode, seed=14600 + splits)
+    k = inputs.growing_keys(k, 20.0)
+    label = f"growing max split {splits} {mode}"
+    log(f"case {label}")
+    o, lse = _run(q, k, v, mode, w.scale, m, splits)
+    want_o, want_lse = oracle.attention_lse(q, k, v, mode, w.scale, m)
+    compare(to64(o), want_o, q.dtype, label)
+    compare_lse(lse, want_lse, q.dtype, label)
