@@ -122,6 +122,9 @@ constexpr int kNumCUs = 256;         // MI355X compute units (automatic split-KV
 // more than kMaxSlack, so P = 2^(s c - m) stays below 2^kMaxSlack (exact in bf16/fp16 and far
 // from overflow in the fp32 sums), and a wave whose rows all keep their max skips the rescale.
 constexpr float kMaxSlack = 8.f;
+#ifndef FA_P2_VALU
+#define FA_P2_VALU 4
+#endif
 #ifndef FA_P1_VALU
 #define FA_P1_VALU 4
 #endif
@@ -670,6 +673,11 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void fa_fwd_kernel(Params
     for (int r = 0; r < 16; ++r) oacc[db][r] = 0.f;
   float m_run = -1e30f;  // finite floor: a fully masked row keeps alpha = 1 and p = 0
   float l_run = 0.f;     // this lane's partial row sum (its 16 keys of each 32-key block)
+  // Head dim 64, packed V^T, 128-row workgroups: the softmax of keys 32..63 runs beside the
+  // first half of the P V matrix instructions (half the matrix work of d = 128 per tile leaves
+  // the first phase short of matrix instructions to hide the vector work under).
+  constexpr bool SPLIT_SM = D == 64 && VPACK && NW == 4;
+  float ps_a = 0.f;      // (SPLIT_SM) row sum of keys 0..31 of the current tile
   const float c = p.c;
 
   // V^T operand (A of O^T += V^T P^T): lane l reads head_dim row 32*db + l%32, unit (ks, hl).
@@ -732,6 +740,19 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void fa_fwd_kernel(Params
   // slots 4..7: keys 16ks + 8 + 4hl + 0..3, the key order of a V^T unit) and returns
   // alpha = 2^(m_old - m_new).  An all -inf tile leaves m_run and l_run unchanged and gives
   // alpha = 1 and P = 0 (m_run is finite).
+  auto exp_block = [&](f32x16 (&s)[NKB], u32x4 (&pk)[PKS], int kb32, float m_new, float (&ps)[2])
+                       __attribute__((always_inline)) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      f32x8 t;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) t[e] = __builtin_amdgcn_exp2f(fmaf(s[kb32][8 * h + e], c, -m_new));
+      const u32x4 pw = pack8<BF16>(t);
+      pk[2 * kb32 + h] = pw;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) ps[e & 1] = dot2_ones<BF16>(pw[e], ps[e & 1]);
+    }
+  };
   auto softmax = [&](f32x16 (&s)[NKB], u32x4 (&pk)[PKS]) __attribute__((always_inline)) {
     // Row max: four independent in-lane chains of 3-input maxima (v_max3_f32) over 8 scores
     // each, then across the two lane halves.
@@ -757,19 +778,19 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void fa_fwd_kernel(Params
     // (v_dot2 against (1, 1)) so numerator and denominator see the same P.
     float ps[2] = {0.f, 0.f};
 #pragma unroll
-    for (int kb32 = 0; kb32 < NKB; ++kb32)
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        f32x8 t;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) t[e] = __builtin_amdgcn_exp2f(fmaf(s[kb32][8 * h + e], c, -m_new));
-        const u32x4 pw = pack8<BF16>(t);
-        pk[2 * kb32 + h] = pw;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) ps[e & 1] = dot2_ones<BF16>(pw[e], ps[e & 1]);
-      }
-    l_run = l_run * alpha + (ps[0] + ps[1]);
+    for (int kb32 = 0; kb32 < (SPLIT_SM ? 1 : NKB); ++kb32)
+      exp_block(s, pk, kb32, m_new, ps);
+    if constexpr (SPLIT_SM) ps_a = ps[0] + ps[1];
+    else l_run = l_run * alpha + (ps[0] + ps[1]);
     return alpha;
+  };
+  // (SPLIT_SM) the rest of the softmax: P of keys 32..63 and the row-sum update.
+  auto softmax_rest = [&](f32x16 (&s)[NKB], u32x4 (&pk)[PKS], float alpha)
+                          __attribute__((always_inline)) {
+    float ps[2] = {0.f, 0.f};
+#pragma unroll
+    for (int kb32 = 1; kb32 < NKB; ++kb32) exp_block(s, pk, kb32, m_run, ps);
+    l_run = l_run * alpha + (ps_a + (ps[0] + ps[1]));
   };
 
   // O = alpha O + V^T P^T (P straight from registers), each V^T operand read PA matrix
@@ -777,22 +798,44 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void fa_fwd_kernel(Params
   // (alpha == 1 in every lane, the common case under the lazy max) skips it as a whole, by one
   // scalar branch on a 64-lane ballot; otherwise every lane multiplies.
   constexpr int PA = FA_PV_AHEAD;
-  auto pv = [&](const unsigned char* vb, const u32x4 (&pk)[PKS], float alpha)
+  auto pv = [&](const unsigned char* vb, u32x4 (&pk)[PKS], float alpha, f32x16 (&s_cur)[NKB])
                 __attribute__((always_inline)) {
     constexpr int N = PKS * NDB;  // i = db * PKS + ks: one accumulator's k-steps back to back
     u32x4 va[PA + 1];
+    if constexpr (!SPLIT_SM) {
 #pragma unroll
-    for (int i = 0; i < PA; ++i) va[i] = v_operand(vb, i % PKS, i / PKS);
+      for (int i = 0; i < PA; ++i) va[i] = v_operand(vb, i % PKS, i / PKS);
+    }
     if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {
 #pragma unroll
       for (int db = 0; db < NDB; ++db)
 #pragma unroll
         for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
     }
+    if constexpr (SPLIT_SM) {
+      // k-steps 0 and 1 (keys 0..31, whose P is ready) for every accumulator, with the softmax
+      // of keys 32..63 interleaved, then k-steps 2 and 3.  Each accumulator still takes its
+      // k-steps in order.
+      constexpr int NH = N / 2;
 #pragma unroll
-    for (int i = 0; i < N; ++i) {
-      if (i + PA < N) va[(i + PA) % (PA + 1)] = v_operand(vb, (i + PA) % PKS, (i + PA) / PKS);
-      oacc[i / PKS] = mfma32<BF16>(va[i % (PA + 1)], pk[i % PKS], oacc[i / PKS]);
+      for (int i = 0; i < NH; ++i)
+        oacc[i % NDB] = mfma32<BF16>(v_operand(vb, i / NDB, i % NDB), pk[i / NDB], oacc[i % NDB]);
+      softmax_rest(s_cur, pk, alpha);
+#pragma unroll
+      for (int i = 0; i < NH; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);          // its V^T operand
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);          // one MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, FA_P2_VALU, 0); // softmax of keys 32..63
+      }
+#pragma unroll
+      for (int i = NH; i < N; ++i)
+        oacc[i % NDB] = mfma32<BF16>(v_operand(vb, i / NDB, i % NDB), pk[i / NDB], oacc[i % NDB]);
+    } else {
+#pragma unroll
+      for (int i = 0; i < N; ++i) {
+        if (i + PA < N) va[(i + PA) % (PA + 1)] = v_operand(vb, (i + PA) % PKS, (i + PA) / PKS);
+        oacc[i / PKS] = mfma32<BF16>(va[i % (PA + 1)], pk[i % PKS], oacc[i / PKS]);
+      }
     }
   };
 
@@ -852,7 +895,7 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void fa_fwd_kernel(Params
       alpha = softmax(s_cur, pk);
       issue_loads();
     }
-    if (live_cur) pv(v_cur, pk, alpha);
+    if (live_cur) pv(v_cur, pk, alpha, s_cur);
     // This wave's K DMA and mask words have landed (the V loads, issued last, may still be in
     // flight: they are consumed in the next iteration; on the packed path the V^T DMA has
     // landed too).
