@@ -69,6 +69,50 @@ def launch_spread(fn, n):
     return {"p10": pick(0.1), "median": pick(0.5), "p90": pick(0.9), "n": n}
 
 
+def clock_under_load(fn, seconds=2.0):
+    """GFX clock (mean over the 8 XCDs) and socket power, read with amd-smi about every 0.4 s
+    while `fn` runs back to back for `seconds` after the timed region: the kernels run at the
+    board's power cap, so the clock they get differs from box to box.  None if amd-smi is not
+    available."""
+    import shutil
+    import subprocess
+    import threading
+    import torch
+    smi = shutil.which("amd-smi")
+    if smi is None:
+        return None
+    samples, stop = [], threading.Event()
+
+    def poll():
+        while not stop.is_set():
+            try:
+                r = subprocess.run([smi, "metric", "-g", "0", "--clock", "--power", "--json"],
+                                   capture_output=True, text=True, timeout=10)
+                d = json.loads(r.stdout)
+                d = d["gpu_data"][0] if isinstance(d, dict) and "gpu_data" in d else d[0]
+                clk = [v["clk"]["value"] for k, v in d["clock"].items() if k.startswith("gfx_")]
+                samples.append((sum(clk) / len(clk), d["power"]["socket_power"]["value"]))
+            except Exception:
+                pass
+            stop.wait(0.4)
+
+    th = threading.Thread(target=poll, daemon=True)
+    t0 = time.time()
+    th.start()
+    while time.time() - t0 < seconds:
+        for _ in range(10):
+            fn()
+        torch.cuda.synchronize()
+    stop.set()
+    th.join(timeout=15)
+    if not samples:
+        return None
+    clk = [c for c, _ in samples]
+    pw = [w for _, w in samples]
+    return {"gfx_mhz_mean": sum(clk) / len(clk), "gfx_mhz_min": min(clk), "gfx_mhz_max": max(clk),
+            "socket_w_max": max(pw), "samples": len(samples), "max_clk_mhz": 2400}
+
+
 MALL_BYTES = 256 << 20   # MI355X Infinity Cache: inputs rotated past it for HBM-bound timings
 
 
@@ -325,6 +369,9 @@ def main():
                          "the key tiles it keeps a key in")
     ap.add_argument("--cpu-budget", type=float, default=12.0,
                     help="seconds of oracle work for the CPU baseline (0 = skip)")
+    ap.add_argument("--clock-seconds", type=float, default=2.0,
+                    help="after the timed region, run the workload this long while amd-smi samples "
+                         "the GFX clock and socket power (0 = skip)")
     ap.add_argument("--no-also", action="store_true",
                     help="skip the timings of the rest of the grid (other shapes, causal, GQA, masked)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -386,6 +433,7 @@ def main():
             fa_fwd(qq, kk, vv, mode=w.mode, scale=w.scale, mask=mm, out=out, tiles=tiles)
     ms = time_launches(main_step, args.steps, args.warmup)
     spread = launch_spread(main_step, args.steps)
+    clock = clock_under_load(main_step, args.clock_seconds) if args.clock_seconds > 0 else None
     if main_step is not step:
         step()   # the output checked against the oracle below is that of the seeded set
         torch.cuda.synchronize()
@@ -445,6 +493,7 @@ def main():
         "warmup": args.warmup,
         "ms_per_step": ms,
         "launch_ms": spread,
+        "clock_under_load": clock,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
