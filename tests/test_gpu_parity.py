@@ -235,3 +235,23 @@ def test_growing_max(mode, D, dtype, B, S, Hq, Hkv, full):
         check_full(q, k, v, mode, w.scale, m, label)
     else:
         check_sampled(q, k, v, mode, w.scale, m, label, seed=w.seed)
+
+
+# Sharp softmax: scaled scores spread over hundreds of exp2 units, so a row's maximum jumps far
+# past the lazy-max slack from tile to tile (in either direction of the scale's sign) and most
+# rows are dominated by one or two keys.
+@pytest.mark.parametrize("scale", [12.0, -12.0])
+@pytest.mark.parametrize("mode,D,dtype,B,S,Hq,Hkv,full", [
+    ("none", 128, "bf16", 1, 4096, 2, 2, False),     # 256-row workgroups
+    ("causal", 128, "bf16", 1, 1100, 4, 2, True),    # 128-row workgroups
+    ("bitmask", 64, "f16", 2, 700, 2, 2, True),
+], ids=lambda x: str(x))
+def test_sharp_softmax(scale, mode, D, dtype, B, S, Hq, Hkv, full):
+    q, k, v = _qkv(B, S, Hq, Hkv, D, dtype, 9500 + S + D)
+    m = _mask(B, Hq, S, 9501 + S) if mode == "bitmask" else None
+    label = f"sharp softmax scale={scale} {mode} d{D} {dtype} B{B} S{S} H{Hq}/{Hkv}"
+    log(f"case {label}")
+    if full:
+        check_full(q, k, v, mode, scale, m, label)
+    else:
+        check_sampled(q, k, v, mode, scale, m, label, seed=9502)
