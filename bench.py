@@ -97,20 +97,23 @@ def clock_under_load(fn, seconds=2.0):
             stop.wait(0.4)
 
     th = threading.Thread(target=poll, daemon=True)
+    for _ in range(50):   # the GPU is busy before the first reading
+        fn()
     t0 = time.time()
     th.start()
     while time.time() - t0 < seconds:
-        for _ in range(10):
+        for _ in range(50):   # enough queued work that the GPU never idles between batches
             fn()
         torch.cuda.synchronize()
     stop.set()
     th.join(timeout=15)
     if not samples:
         return None
-    clk = [c for c, _ in samples]
-    pw = [w for _, w in samples]
-    return {"gfx_mhz_mean": sum(clk) / len(clk), "gfx_mhz_min": min(clk), "gfx_mhz_max": max(clk),
-            "socket_w_max": max(pw), "samples": len(samples), "max_clk_mhz": 2400}
+    clk = sorted(c for c, _ in samples)
+    return {"gfx_mhz_median": clk[len(clk) // 2], "gfx_mhz_min": clk[0], "gfx_mhz_max": clk[-1],
+            "socket_w_max": max(w for _, w in samples),
+            "samples_mhz_w": [[round(c), w] for c, w in samples], "max_clk_mhz": 2400,
+            "note": "instantaneous amd-smi readings, mean over the 8 XCDs each"}
 
 
 MALL_BYTES = 256 << 20   # MI355X Infinity Cache: inputs rotated past it for HBM-bound timings
