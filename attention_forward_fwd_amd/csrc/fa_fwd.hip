@@ -754,19 +754,19 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void fa_fwd_kernel(Params
     }
   };
   auto softmax = [&](f32x16 (&s)[NKB], u32x4 (&pk)[PKS]) __attribute__((always_inline)) {
-    // Row max: four independent in-lane chains of 3-input maxima (v_max3_f32) over 8 scores
-    // each, then across the two lane halves.
-    float mx4[4];
+    // Row max: two independent in-lane chains of 3-input maxima (v_max3_f32), one per 32-key
+    // block (16 scores: seven max3 and one max each), then across the two lane halves.
+    float mx2[NKB];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const f32x16& v = s[(q >> 1) % NKB];
-      const int b0 = 8 * (q & 1);
-      float m = __builtin_fmaxf(__builtin_fmaxf(v[b0], v[b0 + 1]), v[b0 + 2]);
-      m = __builtin_fmaxf(__builtin_fmaxf(m, v[b0 + 3]), v[b0 + 4]);
-      m = __builtin_fmaxf(__builtin_fmaxf(m, v[b0 + 5]), v[b0 + 6]);
-      mx4[q] = __builtin_fmaxf(m, v[b0 + 7]);
+    for (int kb32 = 0; kb32 < NKB; ++kb32) {
+      const f32x16& v = s[kb32];
+      float m = __builtin_fmaxf(__builtin_fmaxf(v[0], v[1]), v[2]);
+#pragma unroll
+      for (int e = 3; e < 15; e += 2) m = __builtin_fmaxf(__builtin_fmaxf(m, v[e]), v[e + 1]);
+      mx2[kb32] = __builtin_fmaxf(m, v[15]);
     }
-    float mx = __builtin_fmaxf(__builtin_fmaxf(mx4[0], mx4[1]), __builtin_fmaxf(mx4[2], mx4[3]));
+    static_assert(NKB == 2, "two 32-key blocks per tile");
+    float mx = __builtin_fmaxf(mx2[0], mx2[1]);
     mx = max_halves(mx);
     // The max moves only past the slack (then straight to the tile's max); otherwise alpha is
     // exactly 1.  A first live tile always moves it off the -1e30 floor; an all -inf tile never.
