@@ -913,19 +913,19 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void fa_fwd_kernel(Params
   bool live_cur;
   f32x16 sA[NKB], sB[NKB];
   // Prologue: Q in registers; V_0, masks 0 and 1, K_0 and K_1 staged, V_1 in registers; S_0
-  // computed.  The K_0 / K_1 DMA and the first V and mask loads are issued right behind the
-  // first Q loads, so their latency overlaps the Q staging; the staging barriers wait only for
-  // the Q loads and LDS accesses (not for those DMAs).
+  // computed.  The Q loads of every staging pass go out first, then the K_0 / K_1 DMA and the
+  // first V and mask loads, so all their latencies overlap the Q staging; the staging barriers
+  // wait only for the Q loads and LDS accesses (not for those DMAs).
   {
-    u32x4 qx[QL];
-    q_load(0, qx);
+    u32x4 qx[QPASS][QL];   // every pass's Q chunks loaded at once (one memory latency)
+#pragma unroll
+    for (int pass = 0; pass < QPASS; ++pass) q_load(pass, qx[pass]);
     dma_tile(kg, tix(0), k_lds0);
     dma_tile(kg, tix(1), k_lds1);
     v_load(tix(0));
     mask_load(tix(0));
 #pragma unroll
     for (int pass = 0; pass < QPASS; ++pass) {
-      if (pass > 0) q_load(pass, qx);
       // (Buffer choices are static, so the compiler can tell these LDS accesses from the DMA
       // into the K buffers and does not wait for it.)  Chunk i of a thread is in the first
       // 64 rows iff i < BN * KC / NT.
@@ -934,8 +934,8 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void fa_fwd_kernel(Params
 #pragma unroll
       for (int i = 0; i < QL; ++i) {
         const int id = tid + NT * i, r = id / KC, c = id % KC;
-        if (i < QHALF) *(u32x4*)(v_lds0 + L::off(r, c)) = qx[i];
-        else *(u32x4*)(v_lds1 + L::off(r - BN, c)) = qx[i];
+        if (i < QHALF) *(u32x4*)(v_lds0 + L::off(r, c)) = qx[pass][i];
+        else *(u32x4*)(v_lds1 + L::off(r - BN, c)) = qx[pass][i];
       }
       __builtin_amdgcn_s_waitcnt(waitcnt_imm(63, 0));
       pipeline_barrier();
