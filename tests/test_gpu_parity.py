@@ -255,3 +255,19 @@ def test_sharp_softmax(scale, mode, D, dtype, B, S, Hq, Hkv, full):
         check_full(q, k, v, mode, scale, m, label)
     else:
         check_sampled(q, k, v, mode, scale, m, label, seed=9502)
+
+
+# Large and uneven GQA groups: a workgroup's rows (position-major, head-minor) then cover only a
+# few positions of many heads, and the group size does not divide the 32-row wave blocks.
+@pytest.mark.parametrize("Hq,Hkv,S,D,dtype", [
+    (64, 1, 70, 128, "bf16"),     # G = 64: 4480 rows per KV head, 256-row workgroups (non-causal)
+    (48, 2, 129, 64, "f16"),      # G = 24
+    (40, 8, 513, 128, "bf16"),    # G = 5
+], ids=lambda x: str(x))
+@pytest.mark.parametrize("mode", ["none", "causal", "bitmask"])
+def test_large_uneven_groups(Hq, Hkv, S, D, dtype, mode):
+    q, k, v = _qkv(1, S, Hq, Hkv, D, dtype, 9700 + Hq + S)
+    m = _mask(1, Hq, S, 9701 + S) if mode == "bitmask" else None
+    label = f"groups {Hq}/{Hkv} {mode} S={S} d{D} {dtype}"
+    log(f"case {label}")
+    check_full(q, k, v, mode, D ** -0.5, m, label)
