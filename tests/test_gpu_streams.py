@@ -63,3 +63,39 @@ def test_two_streams_at_once():
     for r, os_ in zip(ref, outs):
         for o in os_:
             assert torch.equal(o, r), "a call running beside another stream's call changed"
+
+
+def test_calls_from_several_host_threads():
+    # Four host threads, each with its own stream and inputs, call the library at the same time
+    # (ctypes releases the GIL during the call); each result must equal the same call made alone.
+    import threading
+    cases = [_inputs(1, 2048 + 128 * i, 4, 2, 128 if i % 2 == 0 else 64, "bf16" if i % 2 == 0 else "f16",
+                     ("none", "causal", "bitmask", "none")[i], seed=21300 + i) for i in range(4)]
+    log("case four host threads")
+    ref = [fa_fwd(q, k, v, mode=w.mode, scale=w.scale, mask=m) for w, q, k, v, m in cases]
+    torch.cuda.synchronize()
+    outs = [None] * len(cases)
+    errors = []
+
+    def worker(i):
+        try:
+            w, q, k, v, m = cases[i]
+            s = torch.cuda.Stream(device=DEV)
+            s.wait_stream(torch.cuda.default_stream(DEV))
+            with torch.cuda.stream(s):
+                res = [fa_fwd(q, k, v, mode=w.mode, scale=w.scale, mask=m) for _ in range(3)]
+            s.synchronize()
+            outs[i] = res
+        except Exception as e:  # reported in the main thread
+            errors.append(e)
+
+    threads = [threading.Thread(target=worker, args=(i,)) for i in range(len(cases))]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join(timeout=60)
+    assert not errors, errors
+    for r, res in zip(ref, outs):
+        assert res is not None
+        for o in res:
+            assert torch.equal(o, r), "a call made beside calls from other host threads changed"
