@@ -27,7 +27,8 @@ pytestmark = [pytest.mark.gpu,
     lambda: inputs.mha_prefill(4, 8192, False),
     lambda: inputs.mha_prefill(4, 8192, True),
     lambda: inputs.gqa_prefill(4, 8192, 8, True),
-], ids=["mha-none-B4S8192", "mha-causal-B4S8192", "gqa32_8-causal-B4S8192"])
+    lambda: inputs.gqa_prefill(4, 8192, 4, False),
+], ids=["mha-none-B4S8192", "mha-causal-B4S8192", "gqa32_8-causal-B4S8192", "gqa32_4-none-B4S8192"])
 def test_full_tensor(workload):
     w = workload()
     q, k, v = inputs.make_qkv(w)
