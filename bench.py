@@ -9,8 +9,9 @@ shape, every other workload of the grid (other sequence lengths, GQA, the short 
 cases), the default workload through fa_fwd_lse (O plus the per-row log-sum-exp) and the mask
 kernels (byte-mask packing and the tile summary, on the B16 H16 S1000 shape) and a packed-document
 mask on that shape and a sliding-window mask at S32768 (dense walk vs the tile-summary walk), and
-split-KV on small grids (one sequence with one or two heads) are timed alongside and reported
-under "also".
+split-KV on small grids (one sequence with one or two heads), and launch time against sequence
+length on grids of at most one workgroup per CU (the cost of one key-tile iteration), are timed
+alongside and reported under "also".
 
 Prints ONE JSON line.  FLOPs are counted dense, 4*B*Hq*S^2*d, half of that for causal.
 """
@@ -299,6 +300,35 @@ def time_split_kv(inputs, dev, steps):
     return out
 
 
+def time_key_tile_chain(inputs, dev, steps):
+    """Launch time against sequence length on grids of at most one workgroup per CU (B1 H16,
+    inputs resident after the first launch), so the slope is the cost of one 64-key tile
+    iteration with nothing else on the CU to hide its load round trip; the d64 shapes also at
+    B16 (several workgroups per CU) beside them."""
+    import torch
+    from attention_forward_fwd_amd import fa_fwd
+    out = {}
+    for D, dtype, mode, batches in ((64, "f16", "none", (1, 16)), (64, "f16", "bitmask", (1, 16)),
+                                    (128, "bf16", "none", (1,))):
+        for B in batches:
+            us = {}
+            for S in (256, 512, 1024, 2048):
+                w = inputs.Workload("key-tile-chain", dtype, mode, B, S, 16, 16, D,
+                                    seed=6100 + S // 256 + (100 if mode == "bitmask" else 0) + D)
+                q, k, v = inputs.make_qkv_device(w, dev)
+                mask = inputs.make_bitmask_device(w, dev) if mode == "bitmask" else None
+                o = torch.empty_like(q)
+                us[S] = 1e3 * time_launches(lambda: fa_fwd(q, k, v, mode=mode, scale=w.scale,
+                                                           mask=mask, out=o), steps, 5)
+                del q, k, v, o, mask
+            rec = {f"S{S}_us": t for S, t in us.items()}
+            if B == 1:
+                rec["us_per_key_tile_S256_to_S512"] = (us[512] - us[256]) / 4
+                rec["us_per_key_tile_S1024_to_S2048"] = (us[2048] - us[1024]) / 16
+            out[f"d{D} {mode} B{B} H16"] = rec
+    return out
+
+
 def cpu_baseline(w, q, k, v, mask, o_gpu, budget_s):
     """Time the fp64 oracle on a bounded sample of the same workload (row blocks of one head
     at full key length, as many as fit in budget_s) and check the GPU rows it covers."""
@@ -458,6 +488,7 @@ def main():
         also.update(time_document_mask(inputs, dev, 100))
         also["split-kv"] = time_split_kv(inputs, dev, 10)
         also.update(time_sliding_window(inputs, dev, 10))
+        also["key-tile chain"] = time_key_tile_chain(inputs, dev, 100)
 
     bytes_alg = alg_bytes(w)   # Q, K, V (and mask) read + O written
     # HBM bytes per launch measured with rocprofv3 byte counters (profiles/traffic.json); only
