@@ -1135,8 +1135,8 @@ extern "C" {
 
 int fa_abi_version(void) { return FA_ABI_VERSION; }
 
-const char* fa_status_string(int s) {
-  switch (s) {
+const char* fa_status_string(fa_status s) {
+  switch ((int)s) {
     case FA_OK: return "ok";
     case FA_ERR_NULL_PTR: return "null q, k, v, o or lse pointer";
     case FA_ERR_BAD_SHAPE: return "bad shape (non-positive size, heads not divisible, or too large)";
@@ -1144,6 +1144,7 @@ const char* fa_status_string(int s) {
     case FA_ERR_BAD_MASK_MODE: return "unknown mask mode, or bitmask mode without a mask";
     case FA_ERR_BAD_SCALE: return "scale is not finite";
     case FA_ERR_HIP: return "HIP runtime rejected a kernel launch or the workspace allocation";
+    case FA_ERR_WORKSPACE: return "caller workspace smaller than the plan's workspace_bytes or not 256-byte aligned";
     default: return "unknown status";
   }
 }
@@ -1161,6 +1162,7 @@ struct Plan {
   int n_kt, n_rb, G;  // 64-key tiles, 64-row blocks, query heads per KV head
   int64_t n_rt, n_wg; // row tiles per (batch, KV head); workgroups before splitting
   size_t vt_bytes, part_bytes;  // packed V^T workspace, split-KV partials
+  size_t part_off, ws_bytes;    // workspace layout: V^T at 0, partials at part_off (256-aligned)
 };
 
 fa_status make_plan(fa_dtype dtype, fa_mask_mode mask_mode, int batch, int n_q_heads,
@@ -1216,6 +1218,8 @@ fa_status make_plan(fa_dtype dtype, fa_mask_mode mask_mode, int batch, int n_q_h
   pl->n_wg = n_wg;
   pl->vt_bytes = pl->vpack ? (size_t)batch * n_kv_heads * n_kt * tile_bytes : 0;
   pl->part_bytes = n_split > 1 ? (size_t)n_split * batch * seq_len * n_q_heads * (head_dim + 2) * 4 : 0;
+  pl->part_off = (pl->vt_bytes + 255) & ~(size_t)255;
+  pl->ws_bytes = pl->part_bytes ? pl->part_off + pl->part_bytes : pl->vt_bytes;
   return FA_OK;
 }
 
@@ -1223,7 +1227,8 @@ fa_status make_plan(fa_dtype dtype, fa_mask_mode mask_mode, int batch, int n_q_h
 fa_status run_fwd(fa_dtype dtype, fa_mask_mode mask_mode, int batch, int n_q_heads,
                   int n_kv_heads, int seq_len, int head_dim, float scale, const void* q,
                   const void* k, const void* v, const uint32_t* mask, const uint32_t* tiles,
-                  int kv_splits, void* o, float* lse, void* stream) {
+                  int kv_splits, void* o, float* lse, void* user_ws, uint64_t user_ws_bytes,
+                  void* stream) {
   if (!q || !k || !v || !o) {
     // (an unknown dtype or mode is reported first, as the plan would)
     if (dtype != FA_DTYPE_F16 && dtype != FA_DTYPE_BF16) return FA_ERR_UNSUPPORTED;
@@ -1240,6 +1245,9 @@ fa_status run_fwd(fa_dtype dtype, fa_mask_mode mask_mode, int batch, int n_q_hea
   if (!isfinite(scale)) return FA_ERR_BAD_SCALE;
   if (lse && ((uintptr_t)lse & 3u)) return FA_ERR_UNSUPPORTED;
   if (tiles && ((uintptr_t)tiles & 3u)) return FA_ERR_UNSUPPORTED;
+  // A caller's workspace must hold the plan's layout (packed V^T at 0, partials at part_off).
+  if (user_ws && pl.ws_bytes && (((uintptr_t)user_ws & 255u) || user_ws_bytes < pl.ws_bytes))
+    return FA_ERR_WORKSPACE;
   const int nw = pl.nw, n_split = pl.n_split, n_kt = pl.n_kt, n_rb = pl.n_rb, G = pl.G;
   const int64_t n_rt = pl.n_rt, n_wg = pl.n_wg;
 
@@ -1281,26 +1289,23 @@ fa_status run_fwd(fa_dtype dtype, fa_mask_mode mask_mode, int batch, int n_q_hea
   hipStream_t s = (hipStream_t)stream;
   const bool vpack = pl.vpack;
   hipError_t e = hipSuccess;
-  void* ws = nullptr;    // packed V^T
-  void* part = nullptr;  // split-KV partials
-  hipMemPool_t pool = nullptr;
-  if (vpack || n_split > 1) {
+  void* ws = nullptr;  // the pool's workspace, when the caller passes none (freed below)
+  if (pl.ws_bytes && !user_ws) {
+    hipMemPool_t pool = nullptr;
     e = workspace_pool(&pool);
     if (e != hipSuccess) return FA_ERR_HIP;
-  }
-  if (n_split > 1) {
-    e = hipMallocFromPoolAsync(&part, pl.part_bytes, pool, s);
+    e = hipMallocFromPoolAsync(&ws, pl.ws_bytes, pool, s);
     if (e != hipSuccess) return FA_ERR_HIP;
-    p.o_part = (float*)part;
+  }
+  unsigned char* base = (unsigned char*)(user_ws ? user_ws : ws);
+  if (n_split > 1) {
+    p.o_part = (float*)(base + pl.part_off);
     p.ml_part = p.o_part + (size_t)n_split * p.part_rows * head_dim;
     p.lse = nullptr;  // (written by the merge)
   }
   if (vpack) {
-    e = hipMallocFromPoolAsync(&ws, pl.vt_bytes, pool, s);
-    if (e == hipSuccess) {
-      p.vt = (const uint16_t*)ws;
-      e = head_dim == 128 ? launch_pack<128>(p, batch, s) : launch_pack<64>(p, batch, s);
-    }
+    p.vt = (const uint16_t*)base;
+    e = head_dim == 128 ? launch_pack<128>(p, batch, s) : launch_pack<64>(p, batch, s);
   }
   const bool bf16 = dtype == FA_DTYPE_BF16;
   if (e == hipSuccess) {
@@ -1317,11 +1322,9 @@ fa_status run_fwd(fa_dtype dtype, fa_mask_mode mask_mode, int batch, int n_q_hea
     else
       e = head_dim == 128 ? launch_merge<false, 128>(p, lse, s) : launch_merge<false, 64>(p, lse, s);
   }
-  for (void* buf : {ws, part}) {
-    if (buf) {
-      const hipError_t ef = hipFreeAsync(buf, s);
-      if (e == hipSuccess) e = ef;
-    }
+  if (ws) {
+    const hipError_t ef = hipFreeAsync(ws, s);
+    if (e == hipSuccess) e = ef;
   }
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
@@ -1334,7 +1337,7 @@ fa_status fa_fwd(fa_dtype dtype, fa_mask_mode mask_mode, int batch, int n_q_head
                  int n_kv_heads, int seq_len, int head_dim, float scale, const void* q,
                  const void* k, const void* v, const uint32_t* mask, void* o, void* stream) {
   return run_fwd(dtype, mask_mode, batch, n_q_heads, n_kv_heads, seq_len, head_dim, scale, q, k,
-                 v, mask, nullptr, 1, o, nullptr, stream);
+                 v, mask, nullptr, 1, o, nullptr, nullptr, 0, stream);
 }
 
 fa_status fa_fwd_lse(fa_dtype dtype, fa_mask_mode mask_mode, int batch, int n_q_heads,
@@ -1343,7 +1346,7 @@ fa_status fa_fwd_lse(fa_dtype dtype, fa_mask_mode mask_mode, int batch, int n_q_
                      void* stream) {
   if (!lse) return FA_ERR_NULL_PTR;
   return run_fwd(dtype, mask_mode, batch, n_q_heads, n_kv_heads, seq_len, head_dim, scale, q, k,
-                 v, mask, nullptr, 1, o, lse, stream);
+                 v, mask, nullptr, 1, o, lse, nullptr, 0, stream);
 }
 
 fa_status fa_fwd_plan(fa_dtype dtype, fa_mask_mode mask_mode, int batch, int n_q_heads,
@@ -1358,7 +1361,7 @@ fa_status fa_fwd_plan(fa_dtype dtype, fa_mask_mode mask_mode, int batch, int n_q
   plan->packed_v = pl.vpack ? 1 : 0;
   plan->kv_splits = pl.n_split;
   plan->workgroups = pl.n_wg * pl.n_split;
-  plan->workspace_bytes = (uint64_t)(pl.vt_bytes + pl.part_bytes);
+  plan->workspace_bytes = (uint64_t)pl.ws_bytes;
   plan->kernels = 1 + (pl.vpack ? 1 : 0) + (pl.n_split > 1 ? 1 : 0);
   return FA_OK;
 }
@@ -1366,9 +1369,10 @@ fa_status fa_fwd_plan(fa_dtype dtype, fa_mask_mode mask_mode, int batch, int n_q
 fa_status fa_fwd_ex(fa_dtype dtype, fa_mask_mode mask_mode, int batch, int n_q_heads,
                     int n_kv_heads, int seq_len, int head_dim, float scale, const void* q,
                     const void* k, const void* v, const uint32_t* mask, const uint32_t* tiles,
-                    int kv_splits, void* o, float* lse, void* stream) {
+                    int kv_splits, void* o, float* lse, void* workspace,
+                    uint64_t workspace_bytes, void* stream) {
   return run_fwd(dtype, mask_mode, batch, n_q_heads, n_kv_heads, seq_len, head_dim, scale, q, k,
-                 v, mask, tiles, kv_splits, o, lse, stream);
+                 v, mask, tiles, kv_splits, o, lse, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

@@ -19,7 +19,7 @@ FA_DTYPE_F16, FA_DTYPE_BF16 = 0, 1
 MODES = {"none": FA_MASK_NONE, "causal": FA_MASK_CAUSAL, "bitmask": FA_MASK_BITMASK}
 DTYPES = {torch.float16: FA_DTYPE_F16, torch.bfloat16: FA_DTYPE_BF16}
 STATUS = {0: "FA_OK", 1: "FA_ERR_NULL_PTR", 2: "FA_ERR_BAD_SHAPE", 3: "FA_ERR_UNSUPPORTED",
-          4: "FA_ERR_BAD_MASK_MODE", 5: "FA_ERR_BAD_SCALE", 6: "FA_ERR_HIP"}
+          4: "FA_ERR_BAD_MASK_MODE", 5: "FA_ERR_HIP", 6: "FA_ERR_BAD_SCALE", 7: "FA_ERR_WORKSPACE"}
 EXPORTS = ("fa_fwd", "fa_fwd_lse", "fa_fwd_ex", "fa_fwd_plan", "fa_pack_mask", "fa_mask_tiles",
            "fa_status_string", "fa_abi_version")
 
@@ -81,7 +81,7 @@ def load() -> ctypes.CDLL:
         lib.fa_fwd_lse.argtypes = lib.fa_fwd.argtypes[:13] + [ctypes.c_void_p, ctypes.c_void_p]
         lib.fa_fwd_ex.restype = ctypes.c_int
         lib.fa_fwd_ex.argtypes = (lib.fa_fwd.argtypes[:12] + [ctypes.c_void_p, ctypes.c_int]
-                                  + [ctypes.c_void_p] * 3)
+                                  + [ctypes.c_void_p] * 3 + [ctypes.c_uint64, ctypes.c_void_p])
         for name in ("fa_pack_mask", "fa_mask_tiles"):
             f = getattr(lib, name)
             f.restype = ctypes.c_int
@@ -119,13 +119,32 @@ def fa_fwd_lse_raw(dtype: int, mask_mode: int, batch: int, n_q_heads: int, n_kv_
 
 def fa_fwd_ex_raw(dtype: int, mask_mode: int, batch: int, n_q_heads: int, n_kv_heads: int,
                   seq_len: int, head_dim: int, scale: float, q: int, k: int, v: int, mask: int,
-                  tiles: int, kv_splits: int, o: int, lse: int, stream: int) -> int:
+                  tiles: int, kv_splits: int, o: int, lse: int, workspace: int,
+                  workspace_bytes: int, stream: int) -> int:
     """Direct call of fa_fwd_ex with integer pointers (0 = NULL); returns the fa_status code."""
     return load().fa_fwd_ex(dtype, mask_mode, batch, n_q_heads, n_kv_heads, seq_len, head_dim,
-                            ctypes.c_float(scale), q, k, v, mask, tiles, kv_splits, o, lse, stream)
+                            ctypes.c_float(scale), q, k, v, mask, tiles, kv_splits, o, lse,
+                            workspace, workspace_bytes, stream)
 
 
-def _tiles_ptr(tiles, mode, B, Hq, S):
+def _ws_args(workspace, device):
+    """(pointer, bytes) of a caller workspace tensor (any dtype, contiguous, on `device`), or
+    (0, 0) for None (the library's pool)."""
+    if workspace is None:
+        return 0, 0
+    if not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous GPU tensor")
+    _same_gpu("workspace", workspace, device)
+    return workspace.data_ptr(), workspace.numel() * workspace.element_size()
+
+
+def _same_gpu(name, t, device):
+    """Raises unless tensor t is on GPU `device` (the library writes or reads it there)."""
+    if not t.is_cuda or t.device != device:
+        raise ValueError(f"{name} must be a GPU tensor on {device} (got {t.device})")
+
+
+def _tiles_ptr(tiles, mode, B, Hq, S, device):
     if tiles is None:
         return 0
     if mode != "bitmask":
@@ -133,8 +152,9 @@ def _tiles_ptr(tiles, mode, B, Hq, S):
     R = (S + 63) // 64
     shape = (B, Hq, R, (R + 31) // 32)
     if (tuple(tiles.shape) != shape or tiles.dtype not in (torch.int32, getattr(torch, "uint32", torch.int32))
-            or not tiles.is_cuda or not tiles.is_contiguous()):
+            or not tiles.is_contiguous()):
         raise ValueError(f"tiles must be a contiguous 32-bit GPU tensor of shape {shape}")
+    _same_gpu("tiles", tiles, device)
     return tiles.data_ptr()
 
 
@@ -142,9 +162,10 @@ def _args(q, k, v, mode, scale, mask, out):
     """Checks the tensors and returns (B, S, Hq, Hkv, D, scale, mask pointer, out)."""
     if mode not in MODES:
         raise ValueError(f"mode must be one of {sorted(MODES)}")
+    if not q.is_cuda:
+        raise ValueError("q must be a GPU tensor (there is no CPU path)")
     for name, t in (("q", q), ("k", k), ("v", v)):
-        if not t.is_cuda:
-            raise ValueError(f"{name} must be a GPU tensor (there is no CPU path)")
+        _same_gpu(name, t, q.device)
         if not t.is_contiguous():
             raise ValueError(f"{name} must be contiguous")
         if t.dim() != 4:
@@ -164,34 +185,39 @@ def _args(q, k, v, mode, scale, mask, out):
             raise ValueError(f"bitmask mode needs mask of shape {(B, Hq, S, W)}")
         if mask.dtype not in (torch.int32, getattr(torch, "uint32", torch.int32)):
             raise ValueError("mask must hold 32-bit words")
-        if not mask.is_cuda or not mask.is_contiguous():
+        if not mask.is_contiguous():
             raise ValueError("mask must be a contiguous GPU tensor")
+        _same_gpu("mask", mask, q.device)
         mptr = mask.data_ptr()
     if out is None:
         out = torch.empty_like(q)
     elif out.shape != q.shape or out.dtype != q.dtype or not out.is_contiguous():
         raise ValueError("out must be a contiguous tensor like q")
+    else:
+        _same_gpu("out", out, q.device)
     return B, S, Hq, Hkv, D, float(scale), mptr, out
 
 
 def fa_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, mode: str = "none",
            scale: float | None = None, mask: torch.Tensor | None = None,
            out: torch.Tensor | None = None, tiles: torch.Tensor | None = None,
-           kv_splits: int = 1) -> torch.Tensor:
+           kv_splits: int = 1, workspace: torch.Tensor | None = None) -> torch.Tensor:
     """O = softmax(scale Q K^T + mask) V on the GPU (see include/fa.h for the definition).
 
     q [B,S,Hq,D], k/v [B,S,Hkv,D] (bf16 or fp16, contiguous, on one GPU); mask [B,Hq,S,ceil(S/32)]
     int32/uint32 words for mode "bitmask"; tiles (optional, bitmask mode) the mask's per-block
     summary from mask_tiles, so dead 64-key tiles are not loaded; kv_splits: 1 = no split-KV,
-    0 = automatic, 2..16 = that many key ranges per row tile.  Enqueued on torch's current
-    stream; returns o."""
+    0 = automatic, 2..16 = that many key ranges per row tile; workspace (optional) a GPU buffer
+    of at least workspace_bytes(...) bytes used instead of the library's pool.  Enqueued on
+    torch's current stream; returns o."""
     B, S, Hq, Hkv, D, scale, mptr, out = _args(q, k, v, mode, scale, mask, out)
-    tptr = _tiles_ptr(tiles, mode, B, Hq, S)
+    tptr = _tiles_ptr(tiles, mode, B, Hq, S, q.device)
+    wptr, wbytes = _ws_args(workspace, q.device)
     with _OnDevice(q.device) as stream:
-        if tptr or kv_splits != 1:
+        if tptr or kv_splits != 1 or wptr:
             st = fa_fwd_ex_raw(DTYPES[q.dtype], MODES[mode], B, Hq, Hkv, S, D, scale, q.data_ptr(),
                                k.data_ptr(), v.data_ptr(), mptr, tptr, int(kv_splits),
-                               out.data_ptr(), 0, stream)
+                               out.data_ptr(), 0, wptr, wbytes, stream)
         else:
             st = fa_fwd_raw(DTYPES[q.dtype], MODES[mode], B, Hq, Hkv, S, D, scale, q.data_ptr(),
                             k.data_ptr(), v.data_ptr(), mptr, out.data_ptr(), stream)
@@ -203,21 +229,23 @@ def fa_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, mode: str = "none"
 def fa_fwd_lse(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, mode: str = "none",
                scale: float | None = None, mask: torch.Tensor | None = None,
                out: torch.Tensor | None = None, lse: torch.Tensor | None = None,
-               tiles: torch.Tensor | None = None, kv_splits: int = 1):
+               tiles: torch.Tensor | None = None, kv_splits: int = 1,
+               workspace: torch.Tensor | None = None):
     """As fa_fwd, also returning the log-sum-exp of each row's kept scores.
 
     Returns (o, lse) with lse [B, Hq, S] float32 (-inf for a row with no kept key)."""
     B, S, Hq, Hkv, D, scale, mptr, out = _args(q, k, v, mode, scale, mask, out)
-    tptr = _tiles_ptr(tiles, mode, B, Hq, S)
+    tptr = _tiles_ptr(tiles, mode, B, Hq, S, q.device)
     if lse is None:
         lse = torch.empty((B, Hq, S), dtype=torch.float32, device=q.device)
     elif (tuple(lse.shape) != (B, Hq, S) or lse.dtype != torch.float32 or not lse.is_contiguous()
           or lse.device != q.device):
         raise ValueError(f"lse must be a contiguous float32 tensor of shape {(B, Hq, S)} on q's device")
+    wptr, wbytes = _ws_args(workspace, q.device)
     with _OnDevice(q.device) as stream:
         st = fa_fwd_ex_raw(DTYPES[q.dtype], MODES[mode], B, Hq, Hkv, S, D, scale, q.data_ptr(),
                            k.data_ptr(), v.data_ptr(), mptr, tptr, int(kv_splits),
-                           out.data_ptr(), lse.data_ptr(), stream)
+                           out.data_ptr(), lse.data_ptr(), wptr, wbytes, stream)
     if st != 0:
         raise FaError(st, fa_status_string(st))
     return out, lse
@@ -248,6 +276,8 @@ def pack_mask(mask: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tens
         out = torch.empty((B, H, S, W), dtype=torch.int32, device=mask.device)
     elif tuple(out.shape) != (B, H, S, W) or out.dtype != torch.int32 or not out.is_contiguous():
         raise ValueError(f"out must be a contiguous int32 tensor of shape {(B, H, S, W)}")
+    else:
+        _same_gpu("out", out, mask.device)
     with _OnDevice(mask.device) as stream:
         st = fa_pack_mask_raw(B, H, S, mask.data_ptr(), out.data_ptr(), stream)
     if st != 0:
@@ -271,6 +301,8 @@ def mask_tiles(words: torch.Tensor, out: torch.Tensor | None = None) -> torch.Te
         out = torch.empty((B, H, R, TW), dtype=torch.int32, device=words.device)
     elif tuple(out.shape) != (B, H, R, TW) or out.dtype != torch.int32 or not out.is_contiguous():
         raise ValueError(f"out must be a contiguous int32 tensor of shape {(B, H, R, TW)}")
+    else:
+        _same_gpu("out", out, words.device)
     with _OnDevice(words.device) as stream:
         st = fa_mask_tiles_raw(B, H, S, words.data_ptr(), out.data_ptr(), stream)
     if st != 0:
@@ -287,3 +319,12 @@ def fa_fwd_plan(dtype: int, mask_mode: int, batch: int, n_q_heads: int, n_kv_hea
     if st != 0:
         raise FaError(st, fa_status_string(st))
     return {name: getattr(plan, name) for name, _ in FaPlan._fields_}
+
+
+def workspace_bytes(q: torch.Tensor, k: torch.Tensor, mode: str = "none", tiles: bool = False,
+                    kv_splits: int = 1) -> int:
+    """Bytes of device workspace a call with these tensors needs (0 if none): the size of the
+    `workspace` buffer a caller passes to avoid the library's pool."""
+    B, S, Hq, D = q.shape
+    return fa_fwd_plan(DTYPES[q.dtype], MODES[mode], B, Hq, k.shape[2], S, D, tiles,
+                       kv_splits)["workspace_bytes"]

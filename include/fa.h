@@ -43,7 +43,9 @@
  *     (hipMallocFromPoolAsync / hipFreeAsync) from a memory pool the library creates on first
  *     use on each device and keeps until the process ends (memory freed to it is retained);
  *   - otherwise the attention kernel alone.
- * The library keeps no other state.  Calls are safe from several host threads.
+ * A caller that must not allocate passes its own buffer to fa_fwd_ex (`workspace`, sized by
+ * fa_fwd_plan) and no pool is used.  The library keeps no other state.  Calls are safe from
+ * several host threads.
  *
  * Errors: arguments are validated first, synchronously, with no HIP call; on error nothing is
  * enqueued and o is untouched.  A failed workspace allocation or a launch error reported by
@@ -61,7 +63,7 @@
 extern "C" {
 #endif
 
-#define FA_ABI_VERSION 6
+#define FA_ABI_VERSION 7
 
 typedef enum {
   FA_MASK_NONE = 0,     /* every key kept */
@@ -78,8 +80,11 @@ typedef enum {
                                or a tensor larger than 2^31 elements per batch */
   FA_ERR_UNSUPPORTED = 3,   /* head_dim not 64 or 128, unknown dtype, misaligned pointer */
   FA_ERR_BAD_MASK_MODE = 4, /* unknown mask_mode, or FA_MASK_BITMASK with mask == NULL */
-  FA_ERR_BAD_SCALE = 5,     /* scale is NaN or infinite */
-  FA_ERR_HIP = 6            /* the HIP runtime rejected a launch or the workspace allocation */
+  FA_ERR_HIP = 5,           /* the HIP runtime rejected a launch or the workspace allocation */
+  /* codes past the five above: */
+  FA_ERR_BAD_SCALE = 6,     /* scale is NaN or infinite */
+  FA_ERR_WORKSPACE = 7      /* a caller-supplied workspace is smaller than the call needs or not
+                               256-byte aligned */
 } fa_status;
 
 /* Forward attention (see the definition above).  Returns FA_OK once its work is enqueued. */
@@ -106,7 +111,7 @@ fa_status fa_fwd_lse(fa_dtype dtype, fa_mask_mode mask_mode, int batch, int n_q_
                      const void* k, const void* v, const uint32_t* mask, void* o, float* lse,
                      void* stream);
 
-/* The general form: fa_fwd plus three optional arguments.
+/* The general form: fa_fwd plus four optional arguments.
  *   lse    NULL, or as for fa_fwd_lse.
  *   tiles  NULL, or (FA_MASK_BITMASK only) the per-block summary of `mask` made by
  *          fa_mask_tiles below ([batch, n_q_heads, R, TW] uint32, R = ceil(seq_len / 64),
@@ -127,13 +132,23 @@ fa_status fa_fwd_lse(fa_dtype dtype, fa_mask_mode mask_mode, int batch, int n_q_
  *          stated tolerances, not bitwise.  Not combined with tiles.  Workspace: n_splits x
  *          batch x seq_len x n_q_heads x (head_dim + 2) x 4 bytes, stream-ordered from the
  *          same pool as the packed-V buffer (see above); one more kernel is enqueued.
+ *   workspace, workspace_bytes  NULL (workspace_bytes ignored): the call takes its device
+ *          scratch (packed V, split-KV partials) from the library's pool as described above.
+ *          Otherwise a DEVICE buffer owned by the caller, 256-byte aligned, of workspace_bytes
+ *          bytes, at least fa_fwd_plan(...).workspace_bytes: the call then uses it and touches
+ *          no pool, so it allocates nothing.  Its contents on entry do not matter; the enqueued
+ *          work reads and writes it, so it must not be reused or freed before that work has run
+ *          and must not be shared by calls that may run at the same time.  When the plan needs
+ *          no workspace the buffer is not touched.
  * Errors as for fa_fwd, plus: tiles with another mask mode -> FA_ERR_BAD_MASK_MODE;
  * misaligned lse or tiles, R > 2048, kv_splits outside 0..16, or kv_splits > 1 with tiles
- * -> FA_ERR_UNSUPPORTED. */
+ * -> FA_ERR_UNSUPPORTED; a workspace that is too small or misaligned -> FA_ERR_WORKSPACE
+ * (checked with the other arguments, before any HIP call). */
 fa_status fa_fwd_ex(fa_dtype dtype, fa_mask_mode mask_mode, int batch, int n_q_heads,
                     int n_kv_heads, int seq_len, int head_dim, float scale, const void* q,
                     const void* k, const void* v, const uint32_t* mask, const uint32_t* tiles,
-                    int kv_splits, void* o, float* lse, void* stream);
+                    int kv_splits, void* o, float* lse, void* workspace,
+                    uint64_t workspace_bytes, void* stream);
 
 /* The launch plan of a call, from its sizes alone (no pointer, no HIP call, no GPU needed): what
  * fa_fwd_ex with these arguments (with_tiles != 0: a tile summary is passed) would enqueue and
@@ -145,7 +160,8 @@ typedef struct {
   int kv_splits;             /* key-range shares per row tile (1 = no split-KV) */
   int kernels;               /* kernels enqueued: attention, + V pre-pass, + split-KV merge */
   int64_t workgroups;        /* grid of the attention kernel */
-  uint64_t workspace_bytes;  /* device scratch taken stream-ordered from the pool, 0 if none */
+  uint64_t workspace_bytes;  /* device scratch the call needs (from the pool, or the caller's
+                                workspace in fa_fwd_ex), 0 if none */
 } fa_plan;
 
 /* Errors as for fa_fwd_ex's size, mode and kv_splits arguments; plan == NULL ->
@@ -181,8 +197,9 @@ fa_status fa_pack_mask(int batch, int n_heads, int seq_len, const uint8_t* mask_
 fa_status fa_mask_tiles(int batch, int n_heads, int seq_len, const uint32_t* mask_words,
                         uint32_t* tiles, void* stream);
 
-/* Static, NUL-terminated description of a status code (never NULL). */
-const char* fa_status_string(int status);
+/* Static, NUL-terminated description of a status code (never NULL; an unknown code gives
+ * "unknown status"). */
+const char* fa_status_string(fa_status status);
 
 /* FA_ABI_VERSION of the loaded library. */
 int fa_abi_version(void);

@@ -1,7 +1,7 @@
 """Arbitrary-precision brute force of masked softmax attention, for tiny inputs only.
 
 TEST INFRASTRUCTURE, NOT PRODUCT CODE.  It exists to pin the fp64 oracle in
-oracle/attention.py: it is a second, loop-by-loop statement of the same definition in
+oracle/masked_attention.py: it is a second, loop-by-loop statement of the same definition in
 Python's `decimal` arithmetic (50 significant digits), written without numpy, so a slip in
 the vectorised oracle (a transposed operand, a wrong broadcast, a wrong head index) shows up
 as a disagreement far above fp64 rounding.

@@ -53,9 +53,16 @@ def test_no_vendor_math_library_linked():
 
 def test_abi_version_and_status_strings():
     lib = _lib()
-    assert lib.fa_abi_version() == 6
+    assert lib.fa_abi_version() == 7
     header = open(HEADER).read()
-    assert re.search(r"#define FA_ABI_VERSION 6\b", header)
+    assert re.search(r"#define FA_ABI_VERSION 7\b", header)
+    # the first five failure codes in the boundary's order; extensions after them
+    for name, code in (("FA_OK", 0), ("FA_ERR_NULL_PTR", 1), ("FA_ERR_BAD_SHAPE", 2),
+                       ("FA_ERR_UNSUPPORTED", 3), ("FA_ERR_BAD_MASK_MODE", 4), ("FA_ERR_HIP", 5),
+                       ("FA_ERR_BAD_SCALE", 6), ("FA_ERR_WORKSPACE", 7)):
+        assert re.search(rf"\b{name} = {code}\b", header), name
+        assert fab.STATUS[code] == name
+    assert "fa_status_string(fa_status status)" in header
     for code, name in fab.STATUS.items():
         s = fa.fa_status_string(code)
         assert s and isinstance(s, str)
@@ -81,7 +88,7 @@ def _call(**kw):
     (dict(Hq=6, Hkv=4), 2), (dict(S=1 << 20, Hq=128, Hkv=1), 2),
     (dict(D=96), 3), (dict(D=256), 3), (dict(dtype=7), 3), (dict(q=P + 8), 3), (dict(o=P + 2), 3),
     (dict(mode=3), 4), (dict(mode=-1), 4), (dict(mode=2, mask=0), 4), (dict(mode=2, mask=P + 2), 4),
-    (dict(scale=float("nan")), 5), (dict(scale=float("inf")), 5), (dict(scale=float("-inf")), 5),
+    (dict(scale=float("nan")), 6), (dict(scale=float("inf")), 6), (dict(scale=float("-inf")), 6),
 ])
 def test_invalid_arguments_rejected_before_launch(kw, status):
     _lib()
@@ -90,7 +97,7 @@ def test_invalid_arguments_rejected_before_launch(kw, status):
 
 @pytest.mark.parametrize("kw,status", [
     (dict(q=0), 1), (dict(o=0), 1), (dict(D=96), 3), (dict(mode=2, mask=0), 4),
-    (dict(scale=float("nan")), 5), (dict(S=0), 2),
+    (dict(scale=float("nan")), 6), (dict(S=0), 2),
 ])
 def test_lse_entry_invalid_arguments_rejected(kw, status):
     # fa_fwd_lse validates like fa_fwd, given a valid lse pointer
@@ -108,13 +115,42 @@ def test_lse_entry_invalid_arguments_rejected(kw, status):
     (dict(splits=-1), 3), (dict(splits=17), 3), (dict(mode=2, mask=P, tiles=P, splits=2), 3),
 ])
 def test_ex_entry_validates(kw, status):
+    assert _ex(**kw) == status
+
+
+def _ex(**kw):
     _lib()
     a = dict(dtype=1, mode=0, B=1, Hq=2, Hkv=1, S=8, D=128, scale=0.1, q=P, k=P, v=P, mask=0,
-             tiles=0, splits=1, o=P, lse=0)
+             tiles=0, splits=1, o=P, lse=0, ws=0, ws_bytes=0)
     a.update(kw)
-    assert fa.fa_fwd_ex_raw(a["dtype"], a["mode"], a["B"], a["Hq"], a["Hkv"], a["S"], a["D"],
+    return fa.fa_fwd_ex_raw(a["dtype"], a["mode"], a["B"], a["Hq"], a["Hkv"], a["S"], a["D"],
                             a["scale"], a["q"], a["k"], a["v"], a["mask"], a["tiles"],
-                            a["splits"], a["o"], a["lse"], 0) == status
+                            a["splits"], a["o"], a["lse"], a["ws"], a["ws_bytes"], 0)
+
+
+WS_CASE = dict(B=4, Hq=16, Hkv=16, S=8192)   # packed V: the plan needs a workspace
+
+
+@pytest.mark.parametrize("kw", [
+    dict(ws=P, ws_bytes=1),                           # far too small
+    dict(ws=P, ws_bytes=-1 + 4 * 16 * 128 * 64 * 128 * 2),  # one byte short of the plan
+    dict(ws=P + 16, ws_bytes=1 << 30),                # large enough but not 256-byte aligned
+    dict(ws=P, ws_bytes=0),                           # a pointer with no size
+])
+def test_caller_workspace_checked_before_launch(kw):
+    # Rejected synchronously (FA_ERR_WORKSPACE), before any HIP call: these run without a GPU.
+    need = _plan()["workspace_bytes"]
+    assert need == 4 * 16 * 128 * 64 * 128 * 2
+    assert _ex(**WS_CASE, **kw) == 7
+
+
+def test_plan_workspace_layout_with_split_and_packed_v():
+    # packed V^T first, then the split-KV partials at the next 256-byte boundary
+    p = _plan(B=1, Hq=16, Hkv=16, S=1100, splits=2)
+    vt = 16 * 18 * 64 * 128 * 2
+    part = 2 * 1100 * 16 * (128 + 2) * 4
+    assert p["packed_v"] == 1 and p["kv_splits"] == 2
+    assert p["workspace_bytes"] == ((vt + 255) // 256) * 256 + part
 
 
 @pytest.mark.parametrize("lse,status", [(0, 1), (P + 2, 3)])
@@ -146,6 +182,18 @@ def test_python_binding_refuses_cpu_tensors():
         fa.pack_mask(torch.zeros(1, 1, 8, 8, dtype=torch.uint8))
     with pytest.raises(ValueError, match="GPU"):
         fa.mask_tiles(torch.zeros(1, 1, 8, 1, dtype=torch.int32))
+
+
+def test_python_binding_checks_every_tensor_device():
+    # Only q can be checked for "is a GPU tensor" without a GPU here; the same helper checks k,
+    # v, mask, tiles, out and workspace against q's device (a CPU out would hand a host pointer
+    # to a kernel that writes through it).
+    import torch
+    _lib()
+    t = torch.zeros(1, 8, 2, 64, dtype=torch.bfloat16)
+    for name in ("out", "k", "v", "mask", "tiles", "workspace"):
+        with pytest.raises(ValueError, match=f"{name} must be a GPU tensor"):
+            fab._same_gpu(name, t, torch.device("cuda:0"))
 
 
 def test_kernel_launch_stubs_defined():

@@ -12,7 +12,7 @@ import pytest
 import torch
 
 from attention_forward_fwd_amd import fa_fwd, fa_fwd_lse, inputs
-from gpu_util import compare, log, sample_rows, to64
+from gpu_util import compare, log, oracle_rows, sample_rows, to64
 import oracle
 
 pytestmark = pytest.mark.gpu
@@ -92,8 +92,7 @@ def test_lse_prefill_sampled(kind, causal):
     log(f"case lse {w.label}")
     o, lse = _run(q, k, v, w.mode, w.scale)
     rows = sample_rows(w.seq_len, seed=w.seed)
-    want_o, want_lse = oracle.attention_rows(q, k, v, w.mode, w.scale, None, rows=rows,
-                                             return_lse=True)
+    want_o, want_lse = oracle_rows(q, k, v, w.mode, w.scale, None, rows=rows, return_lse=True)
     compare(to64(o[:, torch.as_tensor(rows, device=o.device)]), want_o, q.dtype, w.label)
     compare_lse(lse[:, :, rows], want_lse.transpose(0, 2, 1), q.dtype, w.label)
 

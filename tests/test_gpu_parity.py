@@ -271,3 +271,32 @@ def test_large_uneven_groups(Hq, Hkv, S, D, dtype, mode):
     label = f"groups {Hq}/{Hkv} {mode} S={S} d{D} {dtype}"
     log(f"case {label}")
     check_full(q, k, v, mode, D ** -0.5, m, label)
+
+
+# ----------------------------------------------------------------- per-scenario sweep: long S
+# One sequence (B = 1) at S = 16384 and 32768 for every mode, head dim and dtype, each gated on
+# its own; Hq 4 over Hkv 2 gives 32768-65536 rows per KV head (256-row workgroups, packed V^T).
+# Compared on sampled rows at full key length.
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("mode", ["none", "causal", "bitmask"])
+@pytest.mark.parametrize("S", [16384, 32768])
+def test_long_single_sequence(S, mode, D, dtype):
+    w = inputs.Workload("long-b1", dtype, mode, 1, S, 4, 2, D,
+                        seed=19000 + S // 1024 + 7 * D + (1 if dtype == "f16" else 0)
+                        + {"none": 0, "causal": 2, "bitmask": 4}[mode])
+    q, k, v = inputs.make_qkv(w)
+    m = inputs.make_bitmask(w) if mode == "bitmask" else None
+    log(f"case {w.label}")
+    check_sampled(q, k, v, mode, w.scale, m, w.label, seed=w.seed)
+
+
+# fp16 at the d128 prefill shapes (the benchmark grid runs them in bf16)
+@pytest.mark.parametrize("causal", [False, True], ids=["noncausal", "causal"])
+@pytest.mark.parametrize("B,S", inputs.PREFILL_SHAPES, ids=lambda x: str(x))
+def test_mha_prefill_fp16(B, S, causal):
+    w = inputs.Workload("mha-prefill-fp16", "f16", "causal" if causal else "none", B, S, 16, 16,
+                        128, seed=19500 + S // 1024 + (1 if causal else 0))
+    q, k, v = inputs.make_qkv(w)
+    log(f"case {w.label}")
+    check_sampled(q, k, v, w.mode, w.scale, None, w.label, seed=w.seed)

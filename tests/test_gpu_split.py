@@ -9,7 +9,7 @@ import pytest
 import torch
 
 from attention_forward_fwd_amd import fa_fwd, fa_fwd_lse, inputs
-from gpu_util import compare, log, sample_rows, to64
+from gpu_util import compare, log, oracle_rows, sample_rows, to64
 import oracle
 from test_gpu_lse import compare_lse
 
@@ -54,7 +54,7 @@ def test_split_auto_small_grid(mode):
     log(f"case {label}")
     o, lse = _run(q, k, v, mode, w.scale, None, 0)
     rows = sample_rows(4096, seed=14101)
-    want_o, want_lse = oracle.attention_rows(q, k, v, mode, w.scale, None, rows=rows, return_lse=True)
+    want_o, want_lse = oracle_rows(q, k, v, mode, w.scale, None, rows=rows, return_lse=True)
     compare(to64(o[:, torch.as_tensor(rows, device=o.device)]), want_o, q.dtype, label)
     compare_lse(lse[:, :, rows], want_lse.transpose(0, 2, 1), q.dtype, label)
 
