@@ -1129,6 +1129,32 @@ hipError_t workspace_pool(hipMemPool_t* out) {
   return hipSuccess;
 }
 
+// Device scratch of fa_fwd_noalloc: a file-scope array in every device's copy of this code
+// object (held until the process ends), so that entry point allocates nothing.  Host code never
+// passes `scratch` itself to a kernel (on the host it names a stand-in, not device memory): it
+// resolves each device's address once, with that device current, and uses that pointer.
+constexpr size_t kStaticScratchBytes = (size_t)FA_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices];
+
+hipError_t static_scratch(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!ptr) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
+
 }  // namespace
 
 extern "C" {
@@ -1145,6 +1171,7 @@ const char* fa_status_string(fa_status s) {
     case FA_ERR_BAD_SCALE: return "scale is not finite";
     case FA_ERR_HIP: return "HIP runtime rejected a kernel launch or the workspace allocation";
     case FA_ERR_WORKSPACE: return "caller workspace smaller than the plan's workspace_bytes or not 256-byte aligned";
+    case FA_ERR_SCRATCH_LIMIT: return "the call needs more device scratch than fa_fwd_noalloc's static array holds";
     default: return "unknown status";
   }
 }
@@ -1228,7 +1255,7 @@ fa_status run_fwd(fa_dtype dtype, fa_mask_mode mask_mode, int batch, int n_q_hea
                   int n_kv_heads, int seq_len, int head_dim, float scale, const void* q,
                   const void* k, const void* v, const uint32_t* mask, const uint32_t* tiles,
                   int kv_splits, void* o, float* lse, void* user_ws, uint64_t user_ws_bytes,
-                  void* stream) {
+                  bool use_static_scratch, void* stream) {
   if (!q || !k || !v || !o) {
     // (an unknown dtype or mode is reported first, as the plan would)
     if (dtype != FA_DTYPE_F16 && dtype != FA_DTYPE_BF16) return FA_ERR_UNSUPPORTED;
@@ -1248,6 +1275,11 @@ fa_status run_fwd(fa_dtype dtype, fa_mask_mode mask_mode, int batch, int n_q_hea
   // A caller's workspace must hold the plan's layout (packed V^T at 0, partials at part_off).
   if (user_ws && pl.ws_bytes && (((uintptr_t)user_ws & 255u) || user_ws_bytes < pl.ws_bytes))
     return FA_ERR_WORKSPACE;
+  if (use_static_scratch) {  // (every argument is valid by now: the first HIP call follows)
+    if (pl.ws_bytes > kStaticScratchBytes) return FA_ERR_SCRATCH_LIMIT;
+    if (static_scratch(&user_ws) != hipSuccess) return FA_ERR_HIP;
+    user_ws_bytes = kStaticScratchBytes;
+  }
   const int nw = pl.nw, n_split = pl.n_split, n_kt = pl.n_kt, n_rb = pl.n_rb, G = pl.G;
   const int64_t n_rt = pl.n_rt, n_wg = pl.n_wg;
 
@@ -1337,7 +1369,7 @@ fa_status fa_fwd(fa_dtype dtype, fa_mask_mode mask_mode, int batch, int n_q_head
                  int n_kv_heads, int seq_len, int head_dim, float scale, const void* q,
                  const void* k, const void* v, const uint32_t* mask, void* o, void* stream) {
   return run_fwd(dtype, mask_mode, batch, n_q_heads, n_kv_heads, seq_len, head_dim, scale, q, k,
-                 v, mask, nullptr, 1, o, nullptr, nullptr, 0, stream);
+                 v, mask, nullptr, 1, o, nullptr, nullptr, 0, false, stream);
 }
 
 fa_status fa_fwd_lse(fa_dtype dtype, fa_mask_mode mask_mode, int batch, int n_q_heads,
@@ -1346,7 +1378,7 @@ fa_status fa_fwd_lse(fa_dtype dtype, fa_mask_mode mask_mode, int batch, int n_q_
                      void* stream) {
   if (!lse) return FA_ERR_NULL_PTR;
   return run_fwd(dtype, mask_mode, batch, n_q_heads, n_kv_heads, seq_len, head_dim, scale, q, k,
-                 v, mask, nullptr, 1, o, lse, nullptr, 0, stream);
+                 v, mask, nullptr, 1, o, lse, nullptr, 0, false, stream);
 }
 
 fa_status fa_fwd_plan(fa_dtype dtype, fa_mask_mode mask_mode, int batch, int n_q_heads,
@@ -1372,7 +1404,15 @@ fa_status fa_fwd_ex(fa_dtype dtype, fa_mask_mode mask_mode, int batch, int n_q_h
                     int kv_splits, void* o, float* lse, void* workspace,
                     uint64_t workspace_bytes, void* stream) {
   return run_fwd(dtype, mask_mode, batch, n_q_heads, n_kv_heads, seq_len, head_dim, scale, q, k,
-                 v, mask, tiles, kv_splits, o, lse, workspace, workspace_bytes, stream);
+                 v, mask, tiles, kv_splits, o, lse, workspace, workspace_bytes, false, stream);
+}
+
+fa_status fa_fwd_noalloc(fa_dtype dtype, fa_mask_mode mask_mode, int batch, int n_q_heads,
+                         int n_kv_heads, int seq_len, int head_dim, float scale, const void* q,
+                         const void* k, const void* v, const uint32_t* mask, const uint32_t* tiles,
+                         int kv_splits, void* o, float* lse, void* stream) {
+  return run_fwd(dtype, mask_mode, batch, n_q_heads, n_kv_heads, seq_len, head_dim, scale, q, k,
+                 v, mask, tiles, kv_splits, o, lse, nullptr, 0, true, stream);
 }
 
 }  // extern "C"

@@ -19,9 +19,10 @@ FA_DTYPE_F16, FA_DTYPE_BF16 = 0, 1
 MODES = {"none": FA_MASK_NONE, "causal": FA_MASK_CAUSAL, "bitmask": FA_MASK_BITMASK}
 DTYPES = {torch.float16: FA_DTYPE_F16, torch.bfloat16: FA_DTYPE_BF16}
 STATUS = {0: "FA_OK", 1: "FA_ERR_NULL_PTR", 2: "FA_ERR_BAD_SHAPE", 3: "FA_ERR_UNSUPPORTED",
-          4: "FA_ERR_BAD_MASK_MODE", 5: "FA_ERR_HIP", 6: "FA_ERR_BAD_SCALE", 7: "FA_ERR_WORKSPACE"}
-EXPORTS = ("fa_fwd", "fa_fwd_lse", "fa_fwd_ex", "fa_fwd_plan", "fa_pack_mask", "fa_mask_tiles",
-           "fa_status_string", "fa_abi_version")
+          4: "FA_ERR_BAD_MASK_MODE", 5: "FA_ERR_HIP", 6: "FA_ERR_BAD_SCALE", 7: "FA_ERR_WORKSPACE",
+          8: "FA_ERR_SCRATCH_LIMIT"}
+EXPORTS = ("fa_fwd", "fa_fwd_lse", "fa_fwd_ex", "fa_fwd_noalloc", "fa_fwd_plan", "fa_pack_mask",
+           "fa_mask_tiles", "fa_status_string", "fa_abi_version")
 
 _lib = None
 
@@ -82,6 +83,9 @@ def load() -> ctypes.CDLL:
         lib.fa_fwd_ex.restype = ctypes.c_int
         lib.fa_fwd_ex.argtypes = (lib.fa_fwd.argtypes[:12] + [ctypes.c_void_p, ctypes.c_int]
                                   + [ctypes.c_void_p] * 3 + [ctypes.c_uint64, ctypes.c_void_p])
+        lib.fa_fwd_noalloc.restype = ctypes.c_int
+        lib.fa_fwd_noalloc.argtypes = (lib.fa_fwd.argtypes[:12] + [ctypes.c_void_p, ctypes.c_int]
+                                       + [ctypes.c_void_p] * 3)
         for name in ("fa_pack_mask", "fa_mask_tiles"):
             f = getattr(lib, name)
             f.restype = ctypes.c_int
@@ -125,6 +129,16 @@ def fa_fwd_ex_raw(dtype: int, mask_mode: int, batch: int, n_q_heads: int, n_kv_h
     return load().fa_fwd_ex(dtype, mask_mode, batch, n_q_heads, n_kv_heads, seq_len, head_dim,
                             ctypes.c_float(scale), q, k, v, mask, tiles, kv_splits, o, lse,
                             workspace, workspace_bytes, stream)
+
+
+def fa_fwd_noalloc_raw(dtype: int, mask_mode: int, batch: int, n_q_heads: int, n_kv_heads: int,
+                       seq_len: int, head_dim: int, scale: float, q: int, k: int, v: int,
+                       mask: int, tiles: int, kv_splits: int, o: int, lse: int,
+                       stream: int) -> int:
+    """Direct call of fa_fwd_noalloc with integer pointers (0 = NULL); returns the fa_status."""
+    return load().fa_fwd_noalloc(dtype, mask_mode, batch, n_q_heads, n_kv_heads, seq_len,
+                                 head_dim, ctypes.c_float(scale), q, k, v, mask, tiles, kv_splits,
+                                 o, lse, stream)
 
 
 def _ws_args(workspace, device):
@@ -328,3 +342,31 @@ def workspace_bytes(q: torch.Tensor, k: torch.Tensor, mode: str = "none", tiles:
     B, S, Hq, D = q.shape
     return fa_fwd_plan(DTYPES[q.dtype], MODES[mode], B, Hq, k.shape[2], S, D, tiles,
                        kv_splits)["workspace_bytes"]
+
+
+def fa_fwd_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Tensor,
+                   mode: str = "none", scale: float | None = None,
+                   mask: torch.Tensor | None = None, lse: torch.Tensor | None = None,
+                   tiles: torch.Tensor | None = None, kv_splits: int = 1) -> torch.Tensor:
+    """fa_fwd through fa_fwd_noalloc: nothing is allocated, neither by the library (its device
+    scratch is a static array, FA_NOALLOC_SCRATCH_BYTES per GPU) nor here (out, and lse when
+    wanted, are the caller's).  Calls that may overlap on one GPU share that array and race.
+    Returns out."""
+    if out is None:
+        raise ValueError("fa_fwd_noalloc writes into the caller's out (it allocates nothing)")
+    B, S, Hq, Hkv, D, scale, mptr, out = _args(q, k, v, mode, scale, mask, out)
+    tptr = _tiles_ptr(tiles, mode, B, Hq, S, q.device)
+    lptr = 0
+    if lse is not None:
+        if (tuple(lse.shape) != (B, Hq, S) or lse.dtype != torch.float32
+                or not lse.is_contiguous()):
+            raise ValueError(f"lse must be a contiguous float32 tensor of shape {(B, Hq, S)}")
+        _same_gpu("lse", lse, q.device)
+        lptr = lse.data_ptr()
+    with _OnDevice(q.device) as stream:
+        st = fa_fwd_noalloc_raw(DTYPES[q.dtype], MODES[mode], B, Hq, Hkv, S, D, scale,
+                                q.data_ptr(), k.data_ptr(), v.data_ptr(), mptr, tptr,
+                                int(kv_splits), out.data_ptr(), lptr, stream)
+    if st != 0:
+        raise FaError(st, fa_status_string(st))
+    return out

@@ -63,7 +63,7 @@
 extern "C" {
 #endif
 
-#define FA_ABI_VERSION 7
+#define FA_ABI_VERSION 8
 
 typedef enum {
   FA_MASK_NONE = 0,     /* every key kept */
@@ -83,8 +83,9 @@ typedef enum {
   FA_ERR_HIP = 5,           /* the HIP runtime rejected a launch or the workspace allocation */
   /* codes past the five above: */
   FA_ERR_BAD_SCALE = 6,     /* scale is NaN or infinite */
-  FA_ERR_WORKSPACE = 7      /* a caller-supplied workspace is smaller than the call needs or not
+  FA_ERR_WORKSPACE = 7,     /* a caller-supplied workspace is smaller than the call needs or not
                                256-byte aligned */
+  FA_ERR_SCRATCH_LIMIT = 8  /* fa_fwd_noalloc: the call needs more than FA_NOALLOC_SCRATCH_BYTES */
 } fa_status;
 
 /* Forward attention (see the definition above).  Returns FA_OK once its work is enqueued. */
@@ -149,6 +150,29 @@ fa_status fa_fwd_ex(fa_dtype dtype, fa_mask_mode mask_mode, int batch, int n_q_h
                     const void* k, const void* v, const uint32_t* mask, const uint32_t* tiles,
                     int kv_splits, void* o, float* lse, void* workspace,
                     uint64_t workspace_bytes, void* stream);
+
+/* Device scratch of fa_fwd_noalloc, per GPU: 256 MiB. */
+#define FA_NOALLOC_SCRATCH_BYTES (256u << 20)
+
+/* fa_fwd_ex without any allocation, for callers that cannot allocate device memory: code under
+ * HIP graph capture, serving loops and harnesses that forbid hipMalloc.  Arguments, results and
+ * errors are fa_fwd_ex's (no workspace argument); the device scratch the call needs (the
+ * plan's workspace_bytes: packed V and split-KV partials) is a static array of
+ * FA_NOALLOC_SCRATCH_BYTES in the library's device code, one per GPU it runs on, held until the
+ * process ends.  The caller still allocates q, k, v, mask, tiles, o and lse.
+ *   - A call whose plan needs more scratch than that returns FA_ERR_SCRATCH_LIMIT before any HIP
+ *     call (fa_fwd_plan gives the figure): for example V of more than 256 MiB to pack, or large
+ *     automatic split-KV partials.
+ *   - The first call on a device resolves that device's array address (one HIP query, no
+ *     allocation).  The call never calls hipMalloc, hipFree or an allocating routine.
+ *   - Every call on one GPU shares its array, which keeps the previous call's contents (the
+ *     kernels write every scratch byte they read, so nothing needs clearing).  Calls whose work
+ *     may overlap on one GPU (other streams, other host threads) race on it: order them on one
+ *     stream, or use fa_fwd_ex with a workspace per stream. */
+fa_status fa_fwd_noalloc(fa_dtype dtype, fa_mask_mode mask_mode, int batch, int n_q_heads,
+                         int n_kv_heads, int seq_len, int head_dim, float scale, const void* q,
+                         const void* k, const void* v, const uint32_t* mask, const uint32_t* tiles,
+                         int kv_splits, void* o, float* lse, void* stream);
 
 /* The launch plan of a call, from its sizes alone (no pointer, no HIP call, no GPU needed): what
  * fa_fwd_ex with these arguments (with_tiles != 0: a tile summary is passed) would enqueue and

@@ -53,13 +53,14 @@ def test_no_vendor_math_library_linked():
 
 def test_abi_version_and_status_strings():
     lib = _lib()
-    assert lib.fa_abi_version() == 7
+    assert lib.fa_abi_version() == 8
     header = open(HEADER).read()
-    assert re.search(r"#define FA_ABI_VERSION 7\b", header)
+    assert re.search(r"#define FA_ABI_VERSION 8\b", header)
     # the first five failure codes in the boundary's order; extensions after them
     for name, code in (("FA_OK", 0), ("FA_ERR_NULL_PTR", 1), ("FA_ERR_BAD_SHAPE", 2),
                        ("FA_ERR_UNSUPPORTED", 3), ("FA_ERR_BAD_MASK_MODE", 4), ("FA_ERR_HIP", 5),
-                       ("FA_ERR_BAD_SCALE", 6), ("FA_ERR_WORKSPACE", 7)):
+                       ("FA_ERR_BAD_SCALE", 6), ("FA_ERR_WORKSPACE", 7),
+                       ("FA_ERR_SCRATCH_LIMIT", 8)):
         assert re.search(rf"\b{name} = {code}\b", header), name
         assert fab.STATUS[code] == name
     assert "fa_status_string(fa_status status)" in header
@@ -267,3 +268,36 @@ def test_plan_rejects_what_the_call_rejects(kw, status):
     with pytest.raises(fab.FaError) as ei:
         _plan(**kw)
     assert ei.value.status == status
+
+
+# ---------------------------------------------------------------- fa_fwd_noalloc (validation only)
+def _noalloc(**kw):
+    _lib()
+    a = dict(dtype=1, mode=0, B=1, Hq=2, Hkv=1, S=8, D=128, scale=0.1, q=P, k=P, v=P, mask=0,
+             tiles=0, splits=1, o=P, lse=0)
+    a.update(kw)
+    return fa.fa_fwd_noalloc_raw(a["dtype"], a["mode"], a["B"], a["Hq"], a["Hkv"], a["S"],
+                                 a["D"], a["scale"], a["q"], a["k"], a["v"], a["mask"],
+                                 a["tiles"], a["splits"], a["o"], a["lse"], 0)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=0), 1), (dict(S=0), 2), (dict(D=96), 3), (dict(mode=2, mask=0), 4),
+    (dict(scale=float("nan")), 6), (dict(splits=17), 3), (dict(tiles=P), 4),
+])
+def test_noalloc_validates_like_ex(kw, status):
+    assert _noalloc(**kw) == status
+
+
+def test_noalloc_rejects_more_scratch_than_its_array():
+    # packed V^T is about V's size: B8 S8192 H16 d128 fills the 256 MiB array exactly, B9 is
+    # over it -> status 8, before any HIP call; B4 S8192 (128 MiB) fits.
+    limit = 256 << 20
+    assert re.search(r"#define FA_NOALLOC_SCRATCH_BYTES \(256u << 20\)", open(HEADER).read())
+    assert _plan(B=4)["workspace_bytes"] <= limit
+    assert _plan(B=8, S=8192)["workspace_bytes"] == limit
+    assert _plan(B=9, S=8192)["workspace_bytes"] > limit
+    assert _noalloc(B=9, Hq=16, Hkv=16, S=8192) == 8
+    # split-KV partials of two long heads in 16 shares: 16 x 32768 x 2 x 130 x 4 B > 256 MiB
+    assert _plan(B=1, Hq=2, Hkv=2, S=32768, splits=16)["workspace_bytes"] > limit
+    assert _noalloc(B=1, Hq=2, Hkv=2, S=32768, splits=16) == 8
