@@ -112,8 +112,14 @@ struct Params {
 // rows: half the global->LDS traffic per FLOP), used when a KV head has many rows.
 constexpr int kBN = 64;           // keys per tile
 constexpr int kWide = 8;          // waves of the 256-row workgroup
-constexpr int kWideRows = 4096;   // rows per KV head (S x G) from which it is used
-constexpr int kWideRowsCausal = 8192;   // (causal: its longer diagonal tail favours 128 rows below)
+#ifndef FA_WIDE_ROWS
+#define FA_WIDE_ROWS 4096
+#endif
+#ifndef FA_WIDE_ROWS_CAUSAL
+#define FA_WIDE_ROWS_CAUSAL 8192
+#endif
+constexpr int kWideRows = FA_WIDE_ROWS;   // rows per KV head (S x G) from which it is used
+constexpr int kWideRowsCausal = FA_WIDE_ROWS_CAUSAL;   // (causal: its longer diagonal tail favours 128 rows below)
 constexpr int kPackRowTiles = 8;  // row tiles per KV head from which V is packed once up front
 constexpr int kMaxListTiles = 2048;  // key tiles a workgroup can list from a tile summary
 constexpr int kMaxSplits = 16;       // key ranges per row tile (split-KV)
@@ -122,17 +128,8 @@ constexpr int kNumCUs = 256;         // MI355X compute units (automatic split-KV
 // more than kMaxSlack, so P = 2^(s c - m) stays below 2^kMaxSlack (exact in bf16/fp16 and far
 // from overflow in the fp32 sums), and a wave whose rows all keep their max skips the rescale.
 constexpr float kMaxSlack = 8.f;
-#ifndef FA_P2_VALU
-#define FA_P2_VALU 4
-#endif
-#ifndef FA_P1_VALU
-#define FA_P1_VALU 4
-#endif
 #ifndef FA_QK_AHEAD
 #define FA_QK_AHEAD 3
-#endif
-#ifndef FA_PV_AHEAD
-#define FA_PV_AHEAD 4
 #endif
 
 template <bool BF16>
@@ -673,11 +670,6 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void fa_fwd_kernel(Params
     for (int r = 0; r < 16; ++r) oacc[db][r] = 0.f;
   float m_run = -1e30f;  // finite floor: a fully masked row keeps alpha = 1 and p = 0
   float l_run = 0.f;     // this lane's partial row sum (its 16 keys of each 32-key block)
-  // Head dim 64, packed V^T, 128-row workgroups: the softmax of keys 32..63 runs beside the
-  // first half of the P V matrix instructions (half the matrix work of d = 128 per tile leaves
-  // the first phase short of matrix instructions to hide the vector work under).
-  constexpr bool SPLIT_SM = D == 64 && VPACK && NW == 4;
-  float ps_a = 0.f;      // (SPLIT_SM) row sum of keys 0..31 of the current tile
   const float c = p.c;
 
   // V^T operand (A of O^T += V^T P^T): lane l reads head_dim row 32*db + l%32, unit (ks, hl).
@@ -688,37 +680,65 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void fa_fwd_kernel(Params
     else return *(const u32x4*)(vb + vt_base + ks * Vt<D>::KSS + db * Vt<D>::RGS);
   };
 
-  // ---- Tile pipeline ("tile j" is the j-th tile of the walk: tix(j)).  Iteration j writes
-  // V_{j+1}^T to LDS (from registers loaded one iteration earlier, or by DMA from the packed
-  // tiles) and issues the loads of the mask words of tile j+2 (registers), K_{j+2} (DMA into
-  // LDS) and V_{j+2} (registers), then runs two phases:
-  //   1. S_{j+1} = K_{j+1} Q^T on the matrix cores while the vector units run the masked online
-  //      softmax of S_j (computed one iteration earlier), in one instruction stream that the
-  //      scheduler interleaves (a matrix instruction, an operand read, a few vector
-  //      instructions, repeated);
-  //   2. O = alpha O + V_j^T P_j^T,
-  // and ends at the one workgroup barrier of the tile.  K and V are loaded two tiles ahead (V
-  // lands in registers and is transposed into LDS one iteration later, in phase 1, off the
-  // barrier's path), the mask words one; the keep words of tile j are carried in registers
-  // from iteration j-1, so the mask buffer of tile j can be refilled during iteration j.
-  // Loads past the last tile re-read the last tile (in bounds, never used).
+  // ---- Tile pipeline ("tile j" is the j-th tile of the walk: tix(j)).  Iteration j holds S_j
+  // (computed one iteration earlier) and P_{j-1} (its softmax, one iteration old), and runs one
+  // instruction stream in which three independent pieces of work are interleaved:
+  //   * S_{j+1} = K_{j+1} Q^T                 (matrix cores, K operands from LDS),
+  //   * O += V_{j-1}^T P_{j-1}^T              (matrix cores, V^T operands from LDS, P in registers),
+  //   * the masked online softmax of S_j -> P_j, alpha_j, row sums (vector units),
+  // so every matrix instruction of the tile has vector work of the softmax beside it; then
+  // O *= alpha_j (skipped by a wave whose rows all kept their max) puts O on P_j's scale before
+  // the next iteration adds V_j^T P_j^T.  The iteration also issues the loads of the mask words
+  // of tile j+2 (registers, stored to LDS at its end), K_{j+2} (DMA into LDS) and V_j (DMA of
+  // the packed V^T tile, or the transposed write of V_j from registers loaded one iteration
+  // earlier, and the register load of V_{j+1}), and ends at the one workgroup barrier of the
+  // tile.  The keep words of tile j are carried in registers from iteration j-1, so the mask
+  // buffer of tile j can be refilled during iteration j.  After the last iteration one more
+  // V^T P^T product remains.  Loads past the last tile re-read the last tile (in bounds, never
+  // used).
 
-  // S^T = K Q^T for one tile, each operand read QA matrix instructions ahead.
-  constexpr int QA = FA_QK_AHEAD;
-  auto qk = [&](const unsigned char* kb, f32x16 (&s)[NKB]) __attribute__((always_inline)) {
+  // The matrix instructions of one iteration, in one index space: i < NPV are O^T += V^T P^T
+  // (k-step i / NDB, head_dim block i % NDB: k-step major, so each P register is dead after its
+  // NDB instructions), the next NQK are S^T = K Q^T (k-step t / NKB, 32-key block t % NKB, t =
+  // i - NPV).  Each LDS operand is read AH matrix instructions ahead into a ring of AH + 1
+  // registers indexed by i, across the boundary of the two products.
+  constexpr int NQK = QKS * NKB, NPV = PKS * NDB, NMM = NPV + NQK;
+  constexpr int AH = FA_QK_AHEAD;
+  auto mm_operand = [&](int i, const unsigned char* kb, const unsigned char* vb)
+                        __attribute__((always_inline)) {
+    if (i < NPV) return v_operand(vb, i / NDB, i % NDB);
+    const int t = i - NPV;
+    return *(const u32x4*)(kb + op_addr(t / NKB, t % NKB));
+  };
+  // Operands of instructions i0 .. i0 + AH - 1 (those below iend).
+  auto mm_prefetch = [&](int i0, int iend, u32x4 (&op)[AH + 1], const unsigned char* kb,
+                         const unsigned char* vb) __attribute__((always_inline)) {
 #pragma unroll
-    for (int kb32 = 0; kb32 < NKB; ++kb32)
+    for (int a = 0; a < AH; ++a)
+      if (i0 + a < iend) op[(i0 + a) % (AH + 1)] = mm_operand(i0 + a, kb, vb);
+  };
+  // Instructions i0 .. i1 - 1, reading the operand of i + AH (below iend) before each.
+  auto mm_run = [&](int i0, int i1, int iend, u32x4 (&op)[AH + 1], const unsigned char* kb,
+                    f32x16 (&s)[NKB], const unsigned char* vb, const u32x4 (&pk)[PKS])
+                    __attribute__((always_inline)) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) s[kb32][r] = 0.f;
-    constexpr int N = QKS * NKB;
-    u32x4 ka[QA + 1];
+    for (int i = 0; i < NMM; ++i) {
+      if (i < i0 || i >= i1) continue;
+      if (i + AH < iend) op[(i + AH) % (AH + 1)] = mm_operand(i + AH, kb, vb);
+      const u32x4 a = op[i % (AH + 1)];
+      if (i < NPV) {
+        oacc[i % NDB] = mfma32<BF16>(a, pk[i / NDB], oacc[i % NDB]);
+      } else {
+        const int t = i - NPV;
+        if (t < NKB) {  // first k-step of a 32-key block: accumulate onto zero
+          f32x16 z;
 #pragma unroll
-    for (int i = 0; i < QA; ++i) ka[i] = *(const u32x4*)(kb + op_addr(i / NKB, i % NKB));
-#pragma unroll
-    for (int i = 0; i < N; ++i) {
-      if (i + QA < N)
-        ka[(i + QA) % (QA + 1)] = *(const u32x4*)(kb + op_addr((i + QA) / NKB, (i + QA) % NKB));
-      s[i % NKB] = mfma32<BF16>(ka[i % (QA + 1)], qreg[i / NKB], s[i % NKB]);
+          for (int r = 0; r < 16; ++r) z[r] = 0.f;
+          s[t % NKB] = mfma32<BF16>(a, qreg[t / NKB], z);
+        } else {
+          s[t % NKB] = mfma32<BF16>(a, qreg[t / NKB], s[t % NKB]);
+        }
+      }
     }
   };
 
@@ -735,25 +755,28 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void fa_fwd_kernel(Params
       }
   };
 
-  // Online softmax of one tile's (already masked) scores.  Updates m_run and l_run, writes P
-  // rounded to the input dtype into pk (slots 0..3 of lane half hl: keys 16ks + 4hl + 0..3,
-  // slots 4..7: keys 16ks + 8 + 4hl + 0..3, the key order of a V^T unit) and returns
-  // alpha = 2^(m_old - m_new).  An all -inf tile leaves m_run and l_run unchanged and gives
+  // Online softmax of one tile's (already masked) scores, in two parts so that each can run
+  // beside one of the iteration's two products.  softmax_a: the row max, the new running max
+  // and alpha = 2^(m_old - m_new) (returned), then P of the first SMA 32-key blocks; softmax_b:
+  // P of the rest and the row-sum update.  P is rounded to the input dtype into pk (slots 0..3
+  // of lane half hl: keys 16ks + 4hl + 0..3, slots 4..7: keys 16ks + 8 + 4hl + 0..3, the key
+  // order of a V^T unit).  An all -inf tile leaves m_run and l_run unchanged and gives
   // alpha = 1 and P = 0 (m_run is finite).
-  auto exp_block = [&](f32x16 (&s)[NKB], u32x4 (&pk)[PKS], int kb32, float m_new, float (&ps)[2])
-                       __attribute__((always_inline)) {
+  constexpr int SMA = MODE == kBitmask ? 0 : 1;  // (bitmask: the masking is in part a)
+  float ps_sm[2];
+  auto exp_block = [&](f32x16 (&s)[NKB], u32x4 (&pk)[PKS], int kb32) __attribute__((always_inline)) {
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       f32x8 t;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) t[e] = __builtin_amdgcn_exp2f(fmaf(s[kb32][8 * h + e], c, -m_new));
+      for (int e = 0; e < 8; ++e) t[e] = __builtin_amdgcn_exp2f(fmaf(s[kb32][8 * h + e], c, -m_run));
       const u32x4 pw = pack8<BF16>(t);
       pk[2 * kb32 + h] = pw;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) ps[e & 1] = dot2_ones<BF16>(pw[e], ps[e & 1]);
+      for (int e = 0; e < 4; ++e) ps_sm[e & 1] = dot2_ones<BF16>(pw[e], ps_sm[e & 1]);
     }
   };
-  auto softmax = [&](f32x16 (&s)[NKB], u32x4 (&pk)[PKS]) __attribute__((always_inline)) {
+  auto softmax_a = [&](f32x16 (&s)[NKB], u32x4 (&pk)[PKS]) __attribute__((always_inline)) {
     // Row max: two independent in-lane chains of 3-input maxima (v_max3_f32), one per 32-key
     // block (16 scores: seven max3 and one max each), then across the two lane halves.
     float mx2[NKB];
@@ -776,83 +799,48 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void fa_fwd_kernel(Params
     m_run = m_new;
     // p = 2^(s*c - m), rounded to the input dtype; the row sum adds the rounded values
     // (v_dot2 against (1, 1)) so numerator and denominator see the same P.
-    float ps[2] = {0.f, 0.f};
+    ps_sm[0] = ps_sm[1] = 0.f;
 #pragma unroll
-    for (int kb32 = 0; kb32 < (SPLIT_SM ? 1 : NKB); ++kb32)
-      exp_block(s, pk, kb32, m_new, ps);
-    if constexpr (SPLIT_SM) ps_a = ps[0] + ps[1];
-    else l_run = l_run * alpha + (ps[0] + ps[1]);
+    for (int kb32 = 0; kb32 < SMA; ++kb32) exp_block(s, pk, kb32);
     return alpha;
   };
-  // (SPLIT_SM) the rest of the softmax: P of keys 32..63 and the row-sum update.
-  auto softmax_rest = [&](f32x16 (&s)[NKB], u32x4 (&pk)[PKS], float alpha)
-                          __attribute__((always_inline)) {
-    float ps[2] = {0.f, 0.f};
+  auto softmax_b = [&](f32x16 (&s)[NKB], u32x4 (&pk)[PKS], float alpha) __attribute__((always_inline)) {
 #pragma unroll
-    for (int kb32 = 1; kb32 < NKB; ++kb32) exp_block(s, pk, kb32, m_run, ps);
-    l_run = l_run * alpha + (ps_a + (ps[0] + ps[1]));
+    for (int kb32 = SMA; kb32 < NKB; ++kb32) exp_block(s, pk, kb32);
+    l_run = l_run * alpha + (ps_sm[0] + ps_sm[1]);
   };
 
-  // O = alpha O + V^T P^T (P straight from registers), each V^T operand read PA matrix
-  // instructions ahead.  The rescale has no per-lane branch: a wave whose rows all kept their max
-  // (alpha == 1 in every lane, the common case under the lazy max) skips it as a whole, by one
-  // scalar branch on a 64-lane ballot; otherwise every lane multiplies.
-  constexpr int PA = FA_PV_AHEAD;
-  auto pv = [&](const unsigned char* vb, u32x4 (&pk)[PKS], float alpha, f32x16 (&s_cur)[NKB])
-                __attribute__((always_inline)) {
-    constexpr int N = PKS * NDB;  // i = db * PKS + ks: one accumulator's k-steps back to back
-    u32x4 va[PA + 1];
-    if constexpr (!SPLIT_SM) {
-#pragma unroll
-      for (int i = 0; i < PA; ++i) va[i] = v_operand(vb, i % PKS, i / PKS);
-    }
+  // O = alpha O with no per-lane branch: a wave whose rows all kept their max (alpha == 1 in
+  // every lane, the common case under the lazy max) skips it as a whole, by one scalar branch
+  // on a 64-lane ballot; otherwise every lane multiplies.
+  auto rescale = [&](float alpha) __attribute__((always_inline)) {
     if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {
 #pragma unroll
       for (int db = 0; db < NDB; ++db)
 #pragma unroll
         for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
     }
-    if constexpr (SPLIT_SM) {
-      // k-steps 0 and 1 (keys 0..31, whose P is ready) for every accumulator, with the softmax
-      // of keys 32..63 interleaved, then k-steps 2 and 3.  Each accumulator still takes its
-      // k-steps in order.
-      constexpr int NH = N / 2;
-#pragma unroll
-      for (int i = 0; i < NH; ++i)
-        oacc[i % NDB] = mfma32<BF16>(v_operand(vb, i / NDB, i % NDB), pk[i / NDB], oacc[i % NDB]);
-      softmax_rest(s_cur, pk, alpha);
-#pragma unroll
-      for (int i = 0; i < NH; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);          // its V^T operand
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);          // one MFMA
-        __builtin_amdgcn_sched_group_barrier(0x002, FA_P2_VALU, 0); // softmax of keys 32..63
-      }
-#pragma unroll
-      for (int i = NH; i < N; ++i)
-        oacc[i % NDB] = mfma32<BF16>(v_operand(vb, i / NDB, i % NDB), pk[i / NDB], oacc[i % NDB]);
-    } else {
-#pragma unroll
-      for (int i = 0; i < N; ++i) {
-        if (i + PA < N) va[(i + PA) % (PA + 1)] = v_operand(vb, (i + PA) % PKS, (i + PA) / PKS);
-        oacc[i / PKS] = mfma32<BF16>(va[i % (PA + 1)], pk[i % PKS], oacc[i / PKS]);
-      }
-    }
   };
 
-  // Scheduling pattern of phase 1: the tile's global loads and matrix instructions spread
-  // evenly through the softmax.
+  // Scheduling pattern of the interleaved stream, per part: each matrix instruction with the
+  // operand read of a later one, a share of the tile's global loads and V^T writes (part a),
+  // and VP vector instructions of the softmax (transcendentals included).
   constexpr int NVMEM = (VPACK ? VDMA_PER_WAVE : (VS_THREADS == NT ? 4 : 0)) + DMA_PER_WAVE +
                         (MODE == kBitmask ? 1 : 0);
-  auto phase1_pattern = [&]() __attribute__((always_inline)) {
-    constexpr int N = QKS * NKB;
-    __builtin_amdgcn_sched_group_barrier(0x100, QA, 0);  // first K operands
+  constexpr int VALU_A = 24 + (MODE == kBitmask ? 2 * NKB * 16 : 0) + SMA * 48;
+  constexpr int VALU_B = 4 + (NKB - SMA) * 48;
+  constexpr int VPA = (VALU_A + NPV - 1) / NPV, VPB = (VALU_B + NQK - 1) / NQK;
+  auto stream_pattern = [&](int i0, int i1, auto vp, bool with_loads, bool first)
+                            __attribute__((always_inline)) {
+    if (first) __builtin_amdgcn_sched_group_barrier(0x100, AH, 0);  // first operands
 #pragma unroll
-    for (int i = 0; i < N; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-      if (i + QA < N) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // a later K operand
-      if (i < NVMEM) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // one global load
-      if (!VPACK && i < 8) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);  // one V^T write
-      __builtin_amdgcn_sched_group_barrier(0x002, FA_P1_VALU, 0);  // vector work of the softmax
+    for (int i = 0; i < NMM; ++i) {
+      if (i < i0 || i >= i1) continue;
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one matrix instruction
+      if (i + AH < NMM) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // a later operand
+      if (with_loads && i - i0 < NVMEM) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+      if (with_loads && !VPACK && i - i0 < 8) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x402, decltype(vp)::value, 0);  // softmax (VALU, transcendental)
     }
   };
 
@@ -866,36 +854,61 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void fa_fwd_kernel(Params
     }
   };
 
-  // One pipelined iteration (see above).  s_cur holds S_j, s_nxt receives S_{j+1}; k_fill
-  // receives K_{j+2}, v_fill V_{j+1} (packed path) or V_{j+1}^T from registers.
-  auto iter = [&](int j, Cls& cls_cur, bool& live_cur, f32x16 (&s_cur)[NKB],
-                  f32x16 (&s_nxt)[NKB], const unsigned char* k_nxt, unsigned char* k_fill,
-                  const unsigned char* v_cur, unsigned char* v_fill, const u32* m_nxt,
-                  u32* m_fill) __attribute__((always_inline)) {
-    const int j1 = tix(j + 1), j2 = tix(j + 2);
+  // One pipelined iteration (see above).  s_cur holds S_j, s_nxt receives S_{j+1}; pk_prev holds
+  // P_{j-1} (live_prev: it has a kept key) and receives P_j; k_nxt holds K_{j+1}, k_fill
+  // receives K_{j+2}; v_prev holds V_{j-1}^T, v_fill receives V_j^T; m_nxt holds the mask words
+  // of tile j+1, m_fill receives those of tile j+2.
+  auto iter = [&](int j, Cls& cls_cur, bool& live_cur, bool& live_prev, float& alpha_prev,
+                  f32x16 (&s_cur)[NKB], f32x16 (&s_nxt)[NKB], u32x4 (&pk_prev)[PKS],
+                  const unsigned char* k_nxt,
+                  unsigned char* k_fill, const unsigned char* v_prev, unsigned char* v_fill,
+                  const u32* m_nxt, u32* m_fill) __attribute__((always_inline)) {
+    const int j0 = tix(j), j1 = tix(j + 1), j2 = tix(j + 2);
     auto issue_loads = [&]() __attribute__((always_inline)) {
       mask_load(j2);
       dma_tile(kg, j2, k_fill);
-      v_dma(j1, v_fill);  // (VPACK) V_{j+1}^T straight into LDS
-      v_store(v_fill);    // V_{j+1}^T, from registers loaded during the previous iteration
-      v_load(j2);         // V_{j+2}: lands during this iteration, written in the next
+      v_dma(j0, v_fill);  // (VPACK) V_j^T straight into LDS
+      v_store(v_fill);    // V_j^T, from registers loaded during the previous iteration
+      v_load(j1);         // V_{j+1}: lands during this iteration, written in the next
     };
     Cls cls_nxt = classify(j1, m_nxt);
     const bool live_nxt = wave_live && j + 1 < n_tiles && !cls_nxt.skip;
     retire(cls_nxt, live_nxt);
-    if (!cls_cur.full) mask_scores(cls_cur, s_cur);
+    // (bitmask tiles are never full: their masking is part of the interleaved stream below)
+    if (MODE != kBitmask && !cls_cur.full) mask_scores(cls_cur, s_cur);
     u32x4 pk[PKS];
+    u32x4 op[AH + 1];
     float alpha;
-    if (live_nxt) {
-      issue_loads();
-      qk(k_nxt, s_nxt);
-      alpha = softmax(s_cur, pk);
-      phase1_pattern();
-    } else {  // (loads issued after the softmax here, so they are not hoisted out of the branches)
-      alpha = softmax(s_cur, pk);
-      issue_loads();
+    rescale(alpha_prev);  // O onto P_{j-1}'s scale
+    issue_loads();
+    if (live_nxt || live_prev) {
+      // One interleaved stream in two parts.  Both products always run, so the code has one
+      // path: a skipped tile's P is exactly 0 (its softmax is a no-op), so O += V^T P^T adds
+      // zeros (V^T in LDS is always finite data), and S of a skipped or past-the-end tile is
+      // never used (its keep words are all zero).
+      // part a: O += V_{j-1}^T P_{j-1}^T beside the masking, row max, alpha and the first P
+      mm_prefetch(0, NMM, op, k_nxt, v_prev);
+      mm_run(0, NPV, NMM, op, k_nxt, s_nxt, v_prev, pk_prev);
+      if (MODE == kBitmask) mask_scores(cls_cur, s_cur);
+      alpha = softmax_a(s_cur, pk);
+      stream_pattern(0, NPV, std::integral_constant<int, VPA>{}, true, true);
+      __builtin_amdgcn_sched_barrier(0);
+      // part b: S_{j+1} = K_{j+1} Q^T beside the rest of P and the row sum
+      mm_run(NPV, NMM, NMM, op, k_nxt, s_nxt, v_prev, pk_prev);
+      softmax_b(s_cur, pk, alpha);
+      stream_pattern(NPV, NMM, std::integral_constant<int, VPB>{}, false, false);
+    } else {  // neither product has work (a wave with no valid rows, or two skipped tiles)
+#pragma unroll
+      for (int kb32 = 0; kb32 < NKB; ++kb32)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s_nxt[kb32][r] = 0.f;
+      if (MODE == kBitmask) mask_scores(cls_cur, s_cur);
+      alpha = softmax_a(s_cur, pk);
+      softmax_b(s_cur, pk, alpha);
     }
-    if (live_cur) pv(v_cur, pk, alpha, s_cur);
+    alpha_prev = alpha;
+#pragma unroll
+    for (int t = 0; t < PKS; ++t) pk_prev[t] = pk[t];
     // This wave's K DMA and mask words have landed (the V loads, issued last, may still be in
     // flight: they are consumed in the next iteration; on the packed path the V^T DMA has
     // landed too).
@@ -906,16 +919,21 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void fa_fwd_kernel(Params
     __builtin_amdgcn_s_waitcnt(waitcnt_imm(63, 0));
     pipeline_barrier();
     cls_cur = cls_nxt;
+    live_prev = live_cur;
     live_cur = live_nxt;
   };
 
   Cls cls_cur;
-  bool live_cur;
+  bool live_cur, live_prev = false;
+  float alpha_prev = 1.f;  // alpha of the last softmax, applied to O before the next V^T P^T
   f32x16 sA[NKB], sB[NKB];
-  // Prologue: Q in registers; V_0, masks 0 and 1, K_0 and K_1 staged, V_1 in registers; S_0
-  // computed.  The Q loads of every staging pass go out first, then the K_0 / K_1 DMA and the
-  // first V and mask loads, so all their latencies overlap the Q staging; the staging barriers
-  // wait only for the Q loads and LDS accesses (not for those DMAs).
+  u32x4 pk_prev[PKS];
+#pragma unroll
+  for (int t = 0; t < PKS; ++t) pk_prev[t] = (u32x4){0u, 0u, 0u, 0u};
+  // Prologue: Q in registers; masks 0 and 1, K_0 and K_1 staged, V_0 in registers (register
+  // path); S_0 computed.  The Q loads of every staging pass go out first, then the K_0 / K_1
+  // DMA and the first V and mask loads, so all their latencies overlap the Q staging; the
+  // staging barriers wait only for the Q loads and LDS accesses (not for those DMAs).
   {
     u32x4 qx[QPASS][QL];   // every pass's Q chunks loaded at once (one memory latency)
 #pragma unroll
@@ -952,24 +970,42 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void fa_fwd_kernel(Params
       pipeline_barrier();
     }
   }
-  v_dma(tix(0), v_lds0);
-  __builtin_amdgcn_s_waitcnt(0x0F70);
-  v_store(v_lds0);
+  // Iteration 0 multiplies the V^T buffer v_lds1 (still holding the Q staging, and unwritten
+  // padding) by P_{-1} = 0: fill it with zeros so the product is exactly 0.
+#pragma unroll
+  for (int i = 0; i < (VBUF_BYTES / 16 + NT - 1) / NT; ++i) {
+    const int c = tid + NT * i;
+    if (c < VBUF_BYTES / 16) *(u32x4*)(v_lds1 + 16 * c) = (u32x4){0u, 0u, 0u, 0u};
+  }
+  __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 15));  // K_0, K_1 DMA and the mask words of tile 0
   mask_store(m_lds0);
   mask_load(tix(1));
-  v_load(tix(1));
-  __builtin_amdgcn_s_waitcnt(0x0F70);
+  __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 15));
   mask_store(m_lds1);
   __syncthreads();
   cls_cur = classify(tix(0), m_lds0);
   live_cur = wave_live && !cls_cur.skip;
   retire(cls_cur, live_cur);
-  if (live_cur) qk(k_lds0, sA);
+  if (live_cur) {
+    u32x4 op[AH + 1];
+    mm_prefetch(NPV, NMM, op, k_lds0, v_lds1);
+    mm_run(NPV, NMM, NMM, op, k_lds0, sA, v_lds1, pk_prev);
+  }
   __syncthreads();  // every wave has read K_0 before iteration 0 refills its buffer
   for (int j = 0; j < n_tiles; j += 2) {
-    iter(j, cls_cur, live_cur, sA, sB, k_lds1, k_lds0, v_lds0, v_lds1, m_lds1, m_lds0);
+    iter(j, cls_cur, live_cur, live_prev, alpha_prev, sA, sB, pk_prev, k_lds1, k_lds0, v_lds1,
+         v_lds0, m_lds1, m_lds0);
     if (j + 1 < n_tiles)
-      iter(j + 1, cls_cur, live_cur, sB, sA, k_lds0, k_lds1, v_lds1, v_lds0, m_lds0, m_lds1);
+      iter(j + 1, cls_cur, live_cur, live_prev, alpha_prev, sB, sA, pk_prev, k_lds0, k_lds1,
+           v_lds0, v_lds1, m_lds0, m_lds1);
+  }
+  // The last tile's O += V^T P^T (V_{n-1}^T is in the buffer the last iteration filled).
+  rescale(alpha_prev);
+  if (live_prev) {
+    u32x4 op[AH + 1];
+    const unsigned char* vb = ((n_tiles - 1) & 1) ? v_lds1 : v_lds0;
+    mm_prefetch(0, NPV, op, k_lds0, vb);
+    mm_run(0, NPV, NPV, op, k_lds0, sA, vb, pk_prev);
   }
 
   // ---- Epilogue: O / l (0 for a row with no kept key), rounded, 8-byte stores.
