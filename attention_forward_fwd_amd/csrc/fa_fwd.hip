@@ -29,9 +29,10 @@
 //     touches only the lane's own query.  P never leaves registers: the S^T accumulator layout
 //     is re-used directly as the B operand of the P V product (keys permuted consistently on
 //     both operands).
-//   * Pipeline: per 64-key tile, one instruction stream computes S_{j+1} = K_{j+1} Q^T on the
-//     matrix cores while the vector units run the softmax of S_j, then O += V_j^T P_j^T; loads
-//     are spread through the first phase; one workgroup barrier per tile.
+//   * Pipeline: per 64-key tile, one instruction stream runs O += V_{j-1}^T P_{j-1}^T and
+//     S_{j+1} = K_{j+1} Q^T on the matrix cores while the vector units run the softmax of S_j,
+//     each matrix instruction with a share of the vector work and of the tile's loads; one
+//     workgroup barrier per tile.
 //   * Memory: K tiles go global -> LDS by buffer-load DMA (no registers) into 1 KiB regions of
 //     whole rows, padded so the 128-bit operand reads are conflict-free.  V^T tiles (8 keys of
 //     one head_dim column per 128-bit operand, in the key order of the P registers) either come
@@ -41,13 +42,15 @@
 //     masked, so their probabilities are exactly 0.  Q is staged once through LDS into registers.
 //   * Softmax: exp2 with log2(e) folded into the scale, running max floored at -1e30 so a
 //     fully masked row never makes NaN, masked scores set to -inf with one bit-field extract
-//     and one bit-field insert.  The running max is lazy: it moves only when a tile's max
-//     exceeds it by more than 8 (exp2 domain), so P stays below 2^8 and alpha is exactly 1 on
-//     almost every tile.  The rescale of O has no per-lane branch; a wave in which every lane
-//     has alpha == 1 skips it by one wave-uniform (scalar) branch.
+//     and one bit-field insert.  The running max is lazy and checked after the fact: a tile's
+//     weights are formed against the max as it stands, and only when some lane's sum of them
+//     exceeds 2^15 (which bounds every weight) does the wave take the tile's row max and redo
+//     the tile, rescaling O and the row sum (every lane multiplies: no per-lane branch).  With
+//     it the common tile needs no row max and no rescale.
 //   * Skips: per wave and tile, the keep bits of the wave's rows are voted with a 64-lane
-//     ballot; a tile with no kept bit costs no matrix or softmax work (causal tiles above the
-//     diagonal, empty blocks of a custom mask).  Causal workgroups stop at their last live tile.
+//     ballot.  A skipped tile's weights are exactly 0.  Causal workgroups stop at their last
+//     live tile, and on the diagonal tail (and in the walk over a mask summary) a wave whose
+//     tiles j-1 and j+1 are both dead skips the iteration's matrix work.
 //   * Scheduling: workgroups are remapped so each of the 8 XCDs gets a contiguous range of
 //     tiles (tiles of one KV head share that XCD's L2); causal row tiles run longest first.
 //   * Optional outputs and schedules (fa_fwd_ex): each row's log-sum-exp from the running
@@ -124,10 +127,6 @@ constexpr int kPackRowTiles = 8;  // row tiles per KV head from which V is packe
 constexpr int kMaxListTiles = 2048;  // key tiles a workgroup can list from a tile summary
 constexpr int kMaxSplits = 16;       // key ranges per row tile (split-KV)
 constexpr int kNumCUs = 256;         // MI355X compute units (automatic split-KV sizing)
-// Lazy running max: a row's max (in the exp2 domain) moves only when a tile's max exceeds it by
-// more than kMaxSlack, so P = 2^(s c - m) stays below 2^kMaxSlack (exact in bf16/fp16 and far
-// from overflow in the fp32 sums), and a wave whose rows all keep their max skips the rescale.
-constexpr float kMaxSlack = 8.f;
 #ifndef FA_QK_AHEAD
 #define FA_QK_AHEAD 3
 #endif
@@ -564,14 +563,18 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void fa_fwd_kernel(Params
 
   // ---- K staging by DMA (buffer load into LDS): instruction i of this wave fills region
   // n = i*NW + wave; lane = slot s holds chunk s / RPR of row n*RPR + ((s % RPR) ^ x(chunk)).
+  // One buffer resource over this (batch, KV head)'s S key rows: a row at or past S is outside
+  // it and reads as zeros (its scores are masked in any case); the tile's first row is a scalar
+  // offset, clamped to S so it stays below 2^32.
   const int dma_c = lane / RPR;
   const unsigned dma_off = (unsigned)((lane % RPR) ^ L::x(dma_c)) * row_bytes + dma_c * 16u;
-  auto dma_tile = [&](const uint16_t* __restrict__ src, int j, unsigned char* dst)
-                      __attribute__((always_inline)) {
+  const __amdgpu_buffer_rsrc_t k_rsrc = rows_rsrc(kg, 0, S, kv_stride);
+  auto dma_tile = [&](int j, unsigned char* dst) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < DMA_PER_WAVE; ++i) {
       const int n = i * NW + wave;
-      dma16(rows_rsrc(src, j * BN + n * RPR, S, kv_stride), (lds_void*)(dst + n * RS), dma_off);
+      const unsigned row = (unsigned)min(j * BN + n * RPR, S);
+      dma16(k_rsrc, (lds_void*)(dst + n * RS), dma_off, row * row_bytes);
     }
   };
 
@@ -744,25 +747,33 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void fa_fwd_kernel(Params
 
   // Masked scores -> -inf (bit-field extract of the keep bit + bit-field insert), for tiles
   // that are not full.  A tile with all-zero keep words becomes all -inf, whatever s held.
+  auto mask_block = [&](const Cls& cls, f32x16 (&s)[NKB], int kb32) __attribute__((always_inline)) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int bit = 8 * (r >> 2) + (r & 3);
+      const int keep = ((int)(cls.wsh[kb32] << (31 - bit))) >> 31;
+      s[kb32][r] = __int_as_float((__float_as_int(s[kb32][r]) & keep) | (~keep & (int)0xff800000));
+    }
+  };
   auto mask_scores = [&](const Cls& cls, f32x16 (&s)[NKB]) __attribute__((always_inline)) {
 #pragma unroll
-    for (int kb32 = 0; kb32 < NKB; ++kb32)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int bit = 8 * (r >> 2) + (r & 3);
-        const int keep = ((int)(cls.wsh[kb32] << (31 - bit))) >> 31;
-        s[kb32][r] = __int_as_float((__float_as_int(s[kb32][r]) & keep) | (~keep & (int)0xff800000));
-      }
+    for (int kb32 = 0; kb32 < NKB; ++kb32) mask_block(cls, s, kb32);
   };
 
-  // Online softmax of one tile's (already masked) scores, in two parts so that each can run
-  // beside one of the iteration's two products.  softmax_a: the row max, the new running max
-  // and alpha = 2^(m_old - m_new) (returned), then P of the first SMA 32-key blocks; softmax_b:
-  // P of the rest and the row-sum update.  P is rounded to the input dtype into pk (slots 0..3
-  // of lane half hl: keys 16ks + 4hl + 0..3, slots 4..7: keys 16ks + 8 + 4hl + 0..3, the key
-  // order of a V^T unit).  An all -inf tile leaves m_run and l_run unchanged and gives
-  // alpha = 1 and P = 0 (m_run is finite).
-  constexpr int SMA = MODE == kBitmask ? 0 : 1;  // (bitmask: the masking is in part a)
+  // Online softmax of one tile's (masked) scores with a lazy running max that is checked after
+  // the fact.  Each 32-key block's P = 2^(s c - m) is formed with the running max m as it stands
+  // (softmax_block, one block beside each of the iteration's two products), rounded to the input
+  // dtype into pk (slots 0..3 of lane half hl: keys 16ks + 4hl + 0..3, slots 4..7: keys
+  // 16ks + 8 + 4hl + 0..3, the key order of a V^T unit), and summed per lane from the rounded
+  // values (v_dot2 against (1, 1)), so numerator and denominator see the same P.  The weights
+  // are >= 0, so a lane's sum bounds each of its weights: when no lane's sum exceeds kSumBound
+  // (the common case) the tile is done with alpha = 1 and no row max at all.  Otherwise -- the
+  // first live tile of a row (m still at its -1e30 floor makes the weights infinite), or scores
+  // that rose far above m -- the wave recomputes the tile (softmax_finish): the row max, m_new,
+  // alpha = 2^(m_old - m_new), P and the sums.  Every weight therefore stays below kSumBound
+  // (finite in fp16, far from overflow in the fp32 sums), and O / l and the LSE are the same
+  // function of (m, l) whatever m is.  An all -inf tile gives P = 0 and leaves m and l alone.
+  constexpr float kSumBound = 32768.f;  // 2^15
   float ps_sm[2];
   auto exp_block = [&](f32x16 (&s)[NKB], u32x4 (&pk)[PKS], int kb32) __attribute__((always_inline)) {
 #pragma unroll
@@ -776,50 +787,44 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void fa_fwd_kernel(Params
       for (int e = 0; e < 4; ++e) ps_sm[e & 1] = dot2_ones<BF16>(pw[e], ps_sm[e & 1]);
     }
   };
-  auto softmax_a = [&](f32x16 (&s)[NKB], u32x4 (&pk)[PKS]) __attribute__((always_inline)) {
-    // Row max: two independent in-lane chains of 3-input maxima (v_max3_f32), one per 32-key
-    // block (16 scores: seven max3 and one max each), then across the two lane halves.
-    float mx2[NKB];
-#pragma unroll
-    for (int kb32 = 0; kb32 < NKB; ++kb32) {
-      const f32x16& v = s[kb32];
-      float m = __builtin_fmaxf(__builtin_fmaxf(v[0], v[1]), v[2]);
-#pragma unroll
-      for (int e = 3; e < 15; e += 2) m = __builtin_fmaxf(__builtin_fmaxf(m, v[e]), v[e + 1]);
-      mx2[kb32] = __builtin_fmaxf(m, v[15]);
-    }
-    static_assert(NKB == 2, "two 32-key blocks per tile");
-    float mx = __builtin_fmaxf(mx2[0], mx2[1]);
-    mx = max_halves(mx);
-    // The max moves only past the slack (then straight to the tile's max); otherwise alpha is
-    // exactly 1.  A first live tile always moves it off the -1e30 floor; an all -inf tile never.
-    const float mt = mx * c;
-    const float m_new = mt > m_run + kMaxSlack ? mt : m_run;
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-    m_run = m_new;
-    // p = 2^(s*c - m), rounded to the input dtype; the row sum adds the rounded values
-    // (v_dot2 against (1, 1)) so numerator and denominator see the same P.
-    ps_sm[0] = ps_sm[1] = 0.f;
-#pragma unroll
-    for (int kb32 = 0; kb32 < SMA; ++kb32) exp_block(s, pk, kb32);
-    return alpha;
+  auto softmax_block = [&](const Cls& cls, f32x16 (&s)[NKB], u32x4 (&pk)[PKS], int kb32)
+                           __attribute__((always_inline)) {
+    if (kb32 == 0) ps_sm[0] = ps_sm[1] = 0.f;
+    if (MODE == kBitmask) mask_block(cls, s, kb32);
+    exp_block(s, pk, kb32);
   };
-  auto softmax_b = [&](f32x16 (&s)[NKB], u32x4 (&pk)[PKS], float alpha) __attribute__((always_inline)) {
+  auto softmax_finish = [&](f32x16 (&s)[NKB], u32x4 (&pk)[PKS]) __attribute__((always_inline)) {
+    float ps = ps_sm[0] + ps_sm[1];
+    float alpha = 1.f;
+    if (__builtin_amdgcn_ballot_w64(!(ps <= kSumBound))) {  // (a NaN or infinite sum included)
+      // Row max: two in-lane chains of 3-input maxima (v_max3_f32), one per 32-key block, then
+      // across the two lane halves; the max moves straight to the tile's max.
+      float mx2[NKB];
 #pragma unroll
-    for (int kb32 = SMA; kb32 < NKB; ++kb32) exp_block(s, pk, kb32);
-    l_run = l_run * alpha + (ps_sm[0] + ps_sm[1]);
-  };
-
-  // O = alpha O with no per-lane branch: a wave whose rows all kept their max (alpha == 1 in
-  // every lane, the common case under the lazy max) skips it as a whole, by one scalar branch
-  // on a 64-lane ballot; otherwise every lane multiplies.
-  auto rescale = [&](float alpha) __attribute__((always_inline)) {
-    if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {
+      for (int kb32 = 0; kb32 < NKB; ++kb32) {
+        const f32x16& v = s[kb32];
+        float m = __builtin_fmaxf(__builtin_fmaxf(v[0], v[1]), v[2]);
+#pragma unroll
+        for (int e = 3; e < 15; e += 2) m = __builtin_fmaxf(__builtin_fmaxf(m, v[e]), v[e + 1]);
+        mx2[kb32] = __builtin_fmaxf(m, v[15]);
+      }
+      static_assert(NKB == 2, "two 32-key blocks per tile");
+      const float mx = max_halves(__builtin_fmaxf(mx2[0], mx2[1]));
+      const float m_new = __builtin_fmaxf(m_run, mx * c);
+      alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      m_run = m_new;
+      ps_sm[0] = ps_sm[1] = 0.f;
+#pragma unroll
+      for (int kb32 = 0; kb32 < NKB; ++kb32) exp_block(s, pk, kb32);
+      ps = ps_sm[0] + ps_sm[1];
+      // O (all tiles before this one) onto the new max before this tile's V^T P^T is added;
+      // every lane multiplies (no per-lane branch).
 #pragma unroll
       for (int db = 0; db < NDB; ++db)
 #pragma unroll
         for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
     }
+    l_run = l_run * alpha + ps;
   };
 
   // Scheduling pattern of the interleaved stream, per part: each matrix instruction with the
@@ -827,8 +832,8 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void fa_fwd_kernel(Params
   // and VP vector instructions of the softmax (transcendentals included).
   constexpr int NVMEM = (VPACK ? VDMA_PER_WAVE : (VS_THREADS == NT ? 4 : 0)) + DMA_PER_WAVE +
                         (MODE == kBitmask ? 1 : 0);
-  constexpr int VALU_A = 24 + (MODE == kBitmask ? 2 * NKB * 16 : 0) + SMA * 48;
-  constexpr int VALU_B = 4 + (NKB - SMA) * 48;
+  constexpr int VALU_A = 52 + (MODE == kBitmask ? 32 : 0);  // one block: mask, P, sums
+  constexpr int VALU_B = VALU_A;
   constexpr int VPA = (VALU_A + NPV - 1) / NPV, VPB = (VALU_B + NQK - 1) / NQK;
   auto stream_pattern = [&](int i0, int i1, auto vp, bool with_loads, bool first)
                             __attribute__((always_inline)) {
@@ -858,15 +863,15 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void fa_fwd_kernel(Params
   // P_{j-1} (live_prev: it has a kept key) and receives P_j; k_nxt holds K_{j+1}, k_fill
   // receives K_{j+2}; v_prev holds V_{j-1}^T, v_fill receives V_j^T; m_nxt holds the mask words
   // of tile j+1, m_fill receives those of tile j+2.
-  auto iter = [&](int j, Cls& cls_cur, bool& live_cur, bool& live_prev, float& alpha_prev,
+  auto iter = [&](auto skip, int j, Cls& cls_cur, bool& live_cur, bool& live_prev,
                   f32x16 (&s_cur)[NKB], f32x16 (&s_nxt)[NKB], u32x4 (&pk_prev)[PKS],
-                  const unsigned char* k_nxt,
-                  unsigned char* k_fill, const unsigned char* v_prev, unsigned char* v_fill,
-                  const u32* m_nxt, u32* m_fill) __attribute__((always_inline)) {
+                  const unsigned char* k_nxt, unsigned char* k_fill, const unsigned char* v_prev,
+                  unsigned char* v_fill, const u32* m_nxt, u32* m_fill)
+                  __attribute__((always_inline)) {
     const int j0 = tix(j), j1 = tix(j + 1), j2 = tix(j + 2);
     auto issue_loads = [&]() __attribute__((always_inline)) {
       mask_load(j2);
-      dma_tile(kg, j2, k_fill);
+      dma_tile(j2, k_fill);
       v_dma(j0, v_fill);  // (VPACK) V_j^T straight into LDS
       v_store(v_fill);    // V_j^T, from registers loaded during the previous iteration
       v_load(j1);         // V_{j+1}: lands during this iteration, written in the next
@@ -878,35 +883,35 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void fa_fwd_kernel(Params
     if (MODE != kBitmask && !cls_cur.full) mask_scores(cls_cur, s_cur);
     u32x4 pk[PKS];
     u32x4 op[AH + 1];
-    float alpha;
-    rescale(alpha_prev);  // O onto P_{j-1}'s scale
-    issue_loads();
-    if (live_nxt || live_prev) {
-      // One interleaved stream in two parts.  Both products always run, so the code has one
-      // path: a skipped tile's P is exactly 0 (its softmax is a no-op), so O += V^T P^T adds
-      // zeros (V^T in LDS is always finite data), and S of a skipped or past-the-end tile is
-      // never used (its keep words are all zero).
-      // part a: O += V_{j-1}^T P_{j-1}^T beside the masking, row max, alpha and the first P
+    if (!decltype(skip)::value || live_nxt || live_prev) {
+      issue_loads();  // (in the stream's scheduling region, spread over its first instructions)
+      // One interleaved stream in two parts.  Both products run: when one of the two tiles is
+      // skipped, its P is exactly 0 (so O += V^T P^T adds zeros; V^T in LDS is always finite
+      // data) or its S is never used (its keep words are all zero), and the code keeps one path.
+      // part a: O += V_{j-1}^T P_{j-1}^T beside P of keys 0..31 of tile j
       mm_prefetch(0, NMM, op, k_nxt, v_prev);
       mm_run(0, NPV, NMM, op, k_nxt, s_nxt, v_prev, pk_prev);
-      if (MODE == kBitmask) mask_scores(cls_cur, s_cur);
-      alpha = softmax_a(s_cur, pk);
+      softmax_block(cls_cur, s_cur, pk, 0);
       stream_pattern(0, NPV, std::integral_constant<int, VPA>{}, true, true);
       __builtin_amdgcn_sched_barrier(0);
-      // part b: S_{j+1} = K_{j+1} Q^T beside the rest of P and the row sum
+      // part b: S_{j+1} = K_{j+1} Q^T beside P of keys 32..63
       mm_run(NPV, NMM, NMM, op, k_nxt, s_nxt, v_prev, pk_prev);
-      softmax_b(s_cur, pk, alpha);
+      softmax_block(cls_cur, s_cur, pk, 1);
       stream_pattern(NPV, NMM, std::integral_constant<int, VPB>{}, false, false);
-    } else {  // neither product has work (a wave with no valid rows, or two skipped tiles)
+    } else {
+      // Both neighbouring tiles are skipped by the wave's ballot (no kept key: causal-dead, an
+      // empty mask block, past the end, or a wave with no valid rows): no matrix work.  (S_{j+1}
+      // is not used; define it anyway, so the old contents of its registers are dead here.)
+      issue_loads();
 #pragma unroll
       for (int kb32 = 0; kb32 < NKB; ++kb32)
 #pragma unroll
         for (int r = 0; r < 16; ++r) s_nxt[kb32][r] = 0.f;
-      if (MODE == kBitmask) mask_scores(cls_cur, s_cur);
-      alpha = softmax_a(s_cur, pk);
-      softmax_b(s_cur, pk, alpha);
+      softmax_block(cls_cur, s_cur, pk, 0);
+      softmax_block(cls_cur, s_cur, pk, 1);
     }
-    alpha_prev = alpha;
+    __builtin_amdgcn_sched_barrier(0);
+    softmax_finish(s_cur, pk);
 #pragma unroll
     for (int t = 0; t < PKS; ++t) pk_prev[t] = pk[t];
     // This wave's K DMA and mask words have landed (the V loads, issued last, may still be in
@@ -925,7 +930,6 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void fa_fwd_kernel(Params
 
   Cls cls_cur;
   bool live_cur, live_prev = false;
-  float alpha_prev = 1.f;  // alpha of the last softmax, applied to O before the next V^T P^T
   f32x16 sA[NKB], sB[NKB];
   u32x4 pk_prev[PKS];
 #pragma unroll
@@ -938,8 +942,8 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void fa_fwd_kernel(Params
     u32x4 qx[QPASS][QL];   // every pass's Q chunks loaded at once (one memory latency)
 #pragma unroll
     for (int pass = 0; pass < QPASS; ++pass) q_load(pass, qx[pass]);
-    dma_tile(kg, tix(0), k_lds0);
-    dma_tile(kg, tix(1), k_lds1);
+    dma_tile(tix(0), k_lds0);
+    dma_tile(tix(1), k_lds1);
     v_load(tix(0));
     mask_load(tix(0));
 #pragma unroll
@@ -992,15 +996,32 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void fa_fwd_kernel(Params
     mm_run(NPV, NMM, NMM, op, k_lds0, sA, v_lds1, pk_prev);
   }
   __syncthreads();  // every wave has read K_0 before iteration 0 refills its buffer
-  for (int j = 0; j < n_tiles; j += 2) {
-    iter(j, cls_cur, live_cur, live_prev, alpha_prev, sA, sB, pk_prev, k_lds1, k_lds0, v_lds1,
+  // Two loops over the walk: iterations in which every wave keeps a key in tiles j-1, j and j+1
+  // run without any branch around the matrix work (its cheapest form); the rest skip the matrix
+  // work of a wave whose two neighbouring tiles are both dead by its ballot.  Causal: the tiles
+  // up to the last one wave 0 (the workgroup's first rows) keeps, then the diagonal tail; with a
+  // tile summary (a structured mask): all skipping; otherwise (random masks have no empty tile)
+  // none.
+  int n_fast = n_tiles;
+  if (MODE == kCausal) n_fast = min(n_tiles, min((row0 + 31) / G, S - 1) / BN);
+  if (sparse) n_fast = 0;
+  n_fast &= ~1;
+  const std::integral_constant<bool, false> fast{};
+  const std::integral_constant<bool, true> skipping{};
+  for (int j = 0; j < n_fast; j += 2) {
+    iter(fast, j, cls_cur, live_cur, live_prev, sA, sB, pk_prev, k_lds1, k_lds0, v_lds1, v_lds0,
+         m_lds1, m_lds0);
+    iter(fast, j + 1, cls_cur, live_cur, live_prev, sB, sA, pk_prev, k_lds0, k_lds1, v_lds0,
+         v_lds1, m_lds0, m_lds1);
+  }
+  for (int j = n_fast; j < n_tiles; j += 2) {
+    iter(skipping, j, cls_cur, live_cur, live_prev, sA, sB, pk_prev, k_lds1, k_lds0, v_lds1,
          v_lds0, m_lds1, m_lds0);
     if (j + 1 < n_tiles)
-      iter(j + 1, cls_cur, live_cur, live_prev, alpha_prev, sB, sA, pk_prev, k_lds0, k_lds1,
+      iter(skipping, j + 1, cls_cur, live_cur, live_prev, sB, sA, pk_prev, k_lds0, k_lds1,
            v_lds0, v_lds1, m_lds0, m_lds1);
   }
   // The last tile's O += V^T P^T (V_{n-1}^T is in the buffer the last iteration filled).
-  rescale(alpha_prev);
   if (live_prev) {
     u32x4 op[AH + 1];
     const unsigned char* vb = ((n_tiles - 1) & 1) ? v_lds1 : v_lds0;

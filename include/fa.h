@@ -28,8 +28,9 @@
  * Numerics: Q K^T and P V run on bf16/fp16 matrix cores with fp32 accumulation; softmax runs in
  * fp32 (exp2 with log2(e) folded into the scale); P is rounded to the input dtype before P V;
  * O is rounded to the input dtype (round to nearest even).  The running max a row's weights are
- * taken against may trail its true max by up to 8 (exp2 domain), so weights up to 2^8 are rounded
- * like all others instead of the largest being exactly 1.  A negative scale is handled exactly
+ * taken against may trail its true max (it moves only when a lane's sum of a tile's weights
+ * would pass 2^15), so weights up to 2^15 are rounded like all others instead of the largest
+ * being exactly 1.  A negative scale is handled exactly
  * (the sign is moved onto Q).  Inputs must be finite and |scale * s_j| must stay below 1e30.
  * Results are bitwise deterministic for a given input and device.
  *
