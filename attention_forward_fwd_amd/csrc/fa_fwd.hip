@@ -609,11 +609,15 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void fa_fwd_kernel(Params
   // Mask words (bitmask mode): thread t stages word t / BM of row t % BM for a tile (NKB = 2
   // words per row, so the BM x NKB words of a tile take one load per thread).  The row pointer
   // is clamped to a valid row and the word index to the row length, so the load needs no
-  // branch; words of rows >= S or past the row end are then replaced by 0.
+  // branch; words of rows >= S or past the row end are then replaced by 0.  A tile's words are
+  // loaded three tiles ahead into a register and stored to LDS one iteration later, so each
+  // load (from HBM: every word is read once) has two iterations to arrive.
   static_assert(MODE != kBitmask || BM * NKB == NT, "one mask word per thread and tile");
-  u32 mreg = 0u;      // the loaded word ...
+  u32 mreg = 0u;        // the word most recently loaded ...
   bool mvalid = false;  // ... and whether it is a real word of a valid row (applied at the store,
                         // so no wait for the load is forced where it is issued)
+  u32 mq = 0u;          // the word loaded one iteration earlier (the next one to store)
+  bool mq_valid = false;
   const u32* mrow = nullptr;
   bool mrow_ok = false;
   const int m_row = tid % BM, m_word = tid / BM;
@@ -631,6 +635,13 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void fa_fwd_kernel(Params
   };
   auto mask_store = [&](u32* mb) __attribute__((always_inline)) {
     if (MODE == kBitmask) mb[m_row * NKB + m_word] = mvalid ? mreg : 0u;
+  };
+  auto mask_store_queued = [&](u32* mb) __attribute__((always_inline)) {
+    if (MODE == kBitmask) {
+      mb[m_row * NKB + m_word] = mq_valid ? mq : 0u;
+      mq = mreg;
+      mq_valid = mvalid;
+    }
   };
 
   // Tile class of tile j for this wave: full (no masking), skip (a 64-lane ballot finds no kept
@@ -834,7 +845,10 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void fa_fwd_kernel(Params
                         (MODE == kBitmask ? 1 : 0);
   constexpr int VALU_A = 52 + (MODE == kBitmask ? 32 : 0);  // one block: mask, P, sums
   constexpr int VALU_B = VALU_A;
-  constexpr int VPA = (VALU_A + NPV - 1) / NPV, VPB = (VALU_B + NQK - 1) / NQK;
+#ifndef FA_VP_ADD
+#define FA_VP_ADD 0
+#endif
+  constexpr int VPA = (VALU_A + NPV - 1) / NPV + FA_VP_ADD, VPB = (VALU_B + NQK - 1) / NQK + FA_VP_ADD;
   auto stream_pattern = [&](int i0, int i1, auto vp, bool with_loads, bool first)
                             __attribute__((always_inline)) {
     if (first) __builtin_amdgcn_sched_group_barrier(0x100, AH, 0);  // first operands
@@ -870,10 +884,10 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void fa_fwd_kernel(Params
                   __attribute__((always_inline)) {
     const int j0 = tix(j), j1 = tix(j + 1), j2 = tix(j + 2);
     auto issue_loads = [&]() __attribute__((always_inline)) {
-      mask_load(j2);
       dma_tile(j2, k_fill);
       v_dma(j0, v_fill);  // (VPACK) V_j^T straight into LDS
       v_store(v_fill);    // V_j^T, from registers loaded during the previous iteration
+      mask_load(tix(j + 3));  // (stays in flight past this iteration's wait)
       v_load(j1);         // V_{j+1}: lands during this iteration, written in the next
     };
     Cls cls_nxt = classify(j1, m_nxt);
@@ -883,6 +897,9 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void fa_fwd_kernel(Params
     if (MODE != kBitmask && !cls_cur.full) mask_scores(cls_cur, s_cur);
     u32x4 pk[PKS];
     u32x4 op[AH + 1];
+#ifdef FA_PRIO_A
+    __builtin_amdgcn_s_setprio(FA_PRIO_A);
+#endif
     if (!decltype(skip)::value || live_nxt || live_prev) {
       issue_loads();  // (in the stream's scheduling region, spread over its first instructions)
       // One interleaved stream in two parts.  Both products run: when one of the two tiles is
@@ -895,6 +912,9 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void fa_fwd_kernel(Params
       stream_pattern(0, NPV, std::integral_constant<int, VPA>{}, true, true);
       __builtin_amdgcn_sched_barrier(0);
       // part b: S_{j+1} = K_{j+1} Q^T beside P of keys 32..63
+#ifdef FA_PRIO_B
+      __builtin_amdgcn_s_setprio(FA_PRIO_B);
+#endif
       mm_run(NPV, NMM, NMM, op, k_nxt, s_nxt, v_prev, pk_prev);
       softmax_block(cls_cur, s_cur, pk, 1);
       stream_pattern(NPV, NMM, std::integral_constant<int, VPB>{}, false, false);
@@ -917,9 +937,11 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void fa_fwd_kernel(Params
     // This wave's K DMA and mask words have landed (the V loads, issued last, may still be in
     // flight: they are consumed in the next iteration; on the packed path the V^T DMA has
     // landed too).
-    if (vs_thread) __builtin_amdgcn_s_waitcnt(waitcnt_imm(4, 15));
-    else __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 15));
-    mask_store(m_fill);
+    // (issued last: the mask words of tile j+3, then the register loads of V_{j+1})
+    constexpr int MQ = MODE == kBitmask ? 1 : 0;
+    if (vs_thread) __builtin_amdgcn_s_waitcnt(waitcnt_imm(4 + MQ, 15));
+    else __builtin_amdgcn_s_waitcnt(waitcnt_imm(MQ, 15));
+    mask_store_queued(m_fill);  // the words of tile j+2, loaded during the previous iteration
     // This wave's LDS writes (mask words, V^T) are complete; then meet the other waves.
     __builtin_amdgcn_s_waitcnt(waitcnt_imm(63, 0));
     pipeline_barrier();
@@ -986,6 +1008,9 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void fa_fwd_kernel(Params
   mask_load(tix(1));
   __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 15));
   mask_store(m_lds1);
+  mask_load(tix(2));  // (queued: stored at the end of iteration 0)
+  mq = mreg;
+  mq_valid = mvalid;
   __syncthreads();
   cls_cur = classify(tix(0), m_lds0);
   live_cur = wave_live && !cls_cur.skip;
