@@ -34,12 +34,13 @@
 //     each matrix instruction with a share of the vector work and of the tile's loads; one
 //     workgroup barrier per tile.
 //   * Memory: K tiles go global -> LDS by buffer-load DMA (no registers) into 1 KiB regions of
-//     whole rows, padded so the 128-bit operand reads are conflict-free.  V^T tiles (8 keys of
-//     one head_dim column per 128-bit operand, in the key order of the P registers) either come
-//     the same way from V packed once per call by vt_pack_kernel, or, for short sequences, are
-//     transposed by each workgroup (loads into registers two tiles ahead, byte permutes, LDS
-//     writes).  Buffer resources end at the sequence: key rows past it read as zeros and are
-//     masked, so their probabilities are exactly 0.  Q is staged once through LDS into registers.
+//     whole rows, padded so the 128-bit operand reads are conflict-free.  V reaches the P V
+//     product either as V^T tiles packed once per call by vt_pack_kernel (8 keys of one head_dim
+//     column per 128-bit operand, in the key order of the P registers), copied the same way, or,
+//     when few workgroups share a KV head, as V's own rows copied like K and transposed by the
+//     operand reads (two ds_read_b64_tr_b16 per operand).  Buffer resources end at the sequence:
+//     key rows past it read as zeros and are masked, so their probabilities are exactly 0.  Q is
+//     staged once through LDS into registers.
 //   * Softmax: exp2 with log2(e) folded into the scale, running max floored at -1e30 so a
 //     fully masked row never makes NaN, masked scores set to -inf with one bit-field extract
 //     and one bit-field insert.  The running max is lazy and checked after the fact: a tile's
@@ -123,7 +124,12 @@ constexpr int kWide = 8;          // waves of the 256-row workgroup
 #endif
 constexpr int kWideRows = FA_WIDE_ROWS;   // rows per KV head (S x G) from which it is used
 constexpr int kWideRowsCausal = FA_WIDE_ROWS_CAUSAL;   // (causal: its longer diagonal tail favours 128 rows below)
-constexpr int kPackRowTiles = 8;  // row tiles per KV head from which V is packed once up front
+// Row tiles per KV head from which V is packed once per call (below it, each workgroup reads V's
+// rows through transposing LDS reads: the pre-pass costs more than those reads save).
+#ifndef FA_PACK_ROW_TILES
+#define FA_PACK_ROW_TILES 32
+#endif
+constexpr int kPackRowTiles = FA_PACK_ROW_TILES;
 constexpr int kMaxListTiles = 2048;  // key tiles a workgroup can list from a tile summary
 constexpr int kMaxSplits = 16;       // key ranges per row tile (split-KV)
 constexpr int kNumCUs = 256;         // MI355X compute units (automatic split-KV sizing)
@@ -240,6 +246,8 @@ struct Vt {
 };
 
 typedef __attribute__((address_space(3))) void lds_void;
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
 // DMA of one 16-byte chunk per lane from a buffer resource into LDS: lane i writes dst + 16 i.
 // Compiled in the device pass only: with this builtin in a kernel body, the host pass of the
@@ -276,7 +284,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const uint16_t* base
                                            (int)(rows * (unsigned)row_elems * 2u), 0x00020000);
 }
 
-// Per-thread V staging for one 64-key tile: thread t < THREADS owns column chunk dq (head_dim
+// Per-thread V transpose for one 64-key tile (the packing pre-pass): thread t < THREADS owns column chunk dq (head_dim
 // 8dq..8dq+7) of key quad q (keys 4q..4q+3).  Consecutive lanes take consecutive column chunks
 // of one key row, so every load instruction reads whole rows.  Lanes 16-31 take quad q+2 (same
 // V^T unit, other half) so the two 16-lane halves of a write never share a bank.  The four
@@ -337,9 +345,9 @@ struct VtPack {
   static constexpr int TILE = NREG * 1024;
 };
 
-// Packs V [B, S, Hkv, D] into VtPack tiles: one workgroup per (batch, KV head, key tile), the
-// same register transpose as in-kernel staging, then a linear copy LDS -> memory.  Keys at or
-// past S are zeros.
+// Packs V [B, S, Hkv, D] into VtPack tiles: one workgroup per (batch, KV head, key tile), a
+// register transpose (VStage) into LDS, then a linear copy LDS -> memory.  Keys at or past S
+// are zeros.
 template <int D>
 __global__ __launch_bounds__(256) void vt_pack_kernel(const uint16_t* __restrict__ v,
                                                       uint16_t* __restrict__ vt, int S, int Hkv,
@@ -367,8 +375,8 @@ __global__ __launch_bounds__(256) void vt_pack_kernel(const uint16_t* __restrict
 
 template <bool BF16, int D, int MODE, bool VPACK, int NW>
 __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void fa_fwd_kernel(Params p) {
-  // VPACK: V arrives as packed V^T tiles (vt_pack_kernel) by DMA; otherwise each workgroup
-  // loads and transposes V itself.
+  // VPACK: V arrives as packed V^T tiles (vt_pack_kernel) by DMA; otherwise V's rows arrive by
+  // DMA like K and the operand reads transpose them.
   constexpr int BM = NW * 32, BN = kBN, NT = NW * 64;
   static_assert(NW == 4 || NW == 8, "workgroup shape");
   constexpr int KC = D / 8;        // 16-byte chunks per row
@@ -380,8 +388,7 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void fa_fwd_kernel(Params
   constexpr int RPR = L::RPR, RS = L::RS;
   constexpr int NREG = BN / RPR;     // regions per tile
   constexpr int T_BYTES = NREG * RS; // one K tile (BN rows)
-  constexpr int VT_BYTES = VPACK ? VtPack<D>::TILE : Vt<D>::BYTES;  // one transposed V tile
-  constexpr int VS_THREADS = VStage<D, NT>::THREADS;  // V staging: one key quad x one column chunk each
+  constexpr int VT_BYTES = VPACK ? VtPack<D>::TILE : T_BYTES;  // one packed V^T tile, or V rows
   constexpr int M_WORDS = MODE == kBitmask ? BM * NKB : 1;
   constexpr int DMA_PER_WAVE = NREG / NW;             // one region per DMA instruction
   constexpr int QROWS = 2 * BN;                       // Q rows staged per pass (two K buffers)
@@ -389,7 +396,7 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void fa_fwd_kernel(Params
   constexpr int QL = QROWS * KC / NT;                 // Q chunks staged per thread and pass
   static_assert(BM % QROWS == 0 && QL >= 1, "Q staging uses the two K buffers, BN rows each");
   static_assert(DMA_PER_WAVE * NW == NREG && QL * NT == QROWS * KC, "load split");
-  static_assert(BN == 64 && VS_THREADS <= NT, "V staging covers a 64-key tile");
+  static_assert(BN == 64, "64-key tiles");
 
   // Separate arrays (not one array indexed by buffer) so the compiler can tell the DMA into one
   // buffer from LDS reads of another and does not wait for the DMA before those reads.
@@ -569,40 +576,36 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void fa_fwd_kernel(Params
   const int dma_c = lane / RPR;
   const unsigned dma_off = (unsigned)((lane % RPR) ^ L::x(dma_c)) * row_bytes + dma_c * 16u;
   const __amdgpu_buffer_rsrc_t k_rsrc = rows_rsrc(kg, 0, S, kv_stride);
-  auto dma_tile = [&](int j, unsigned char* dst) __attribute__((always_inline)) {
+  auto dma_rows = [&](__amdgpu_buffer_rsrc_t rsrc, int j, unsigned char* dst) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < DMA_PER_WAVE; ++i) {
       const int n = i * NW + wave;
       const unsigned row = (unsigned)min(j * BN + n * RPR, S);
-      dma16(k_rsrc, (lds_void*)(dst + n * RS), dma_off, row * row_bytes);
+      dma16(rsrc, (lds_void*)(dst + n * RS), dma_off, row * row_bytes);
     }
   };
+  auto dma_tile = [&](int j, unsigned char* dst) __attribute__((always_inline)) { dma_rows(k_rsrc, j, dst); };
 
   // ---- V staging.  VPACK: one DMA instruction per 1 KiB region of a packed V^T tile (lane i
-  // -> 16 i), instruction i of this wave taking region i*NW + wave.  Otherwise: loads into
-  // registers, transposed into LDS by VStage.
-  const VStage<D, NT> vst(tid, row_bytes);
-  const bool vs_thread = !VPACK && vst.active;
-  u32x4 vstage[4];
-  auto v_load = [&](int j) __attribute__((always_inline)) {
-    if (!VPACK) vst.load(vstage, vg, j * BN, S, kv_stride);
-  };
-  auto v_store = [&](unsigned char* vt) __attribute__((always_inline)) {
-    if (!VPACK) vst.store(vstage, vt);
-  };
-  constexpr int VDMA_PER_WAVE = VtPack<D>::NREG / NW;
-  static_assert(VDMA_PER_WAVE * NW == VtPack<D>::NREG, "packed V^T regions split over waves");
-  const __amdgpu_buffer_rsrc_t vt_rsrc = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(VPACK ? p.vt + (size_t)bh * p.n_kt * (VtPack<D>::TILE / 2) : p.v), (short)0,
-      VPACK ? p.n_kt * VtPack<D>::TILE : 0, 0x00020000);
+  // -> 16 i), instruction i of this wave taking region i*NW + wave.  Otherwise V's rows by DMA
+  // into the K layout, like K (the operand reads transpose them).
+  constexpr int VDMA_PER_WAVE = VPACK ? VtPack<D>::NREG / NW : DMA_PER_WAVE;
+  static_assert(!VPACK || VDMA_PER_WAVE * NW == VtPack<D>::NREG, "packed V^T regions split over waves");
+  const __amdgpu_buffer_rsrc_t v_rsrc =
+      VPACK ? __builtin_amdgcn_make_buffer_rsrc(
+                  (void*)(p.vt + (size_t)bh * p.n_kt * (VtPack<D>::TILE / 2)), (short)0,
+                  p.n_kt * VtPack<D>::TILE, 0x00020000)
+            : rows_rsrc(vg, 0, S, kv_stride);
   auto v_dma = [&](int j, unsigned char* dst) __attribute__((always_inline)) {
-    if (VPACK) {
+    if constexpr (VPACK) {
 #pragma unroll
       for (int i = 0; i < VDMA_PER_WAVE; ++i) {
         const int n = i * NW + wave;
-        dma16(vt_rsrc, (lds_void*)(dst + n * 1024), lane * 16u + n * 1024u,
+        dma16(v_rsrc, (lds_void*)(dst + n * 1024), lane * 16u + n * 1024u,
               (unsigned)(j * VtPack<D>::TILE));
       }
+    } else {
+      dma_rows(v_rsrc, j, dst);
     }
   };
 
@@ -686,12 +689,28 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void fa_fwd_kernel(Params
   float l_run = 0.f;     // this lane's partial row sum (its 16 keys of each 32-key block)
   const float c = p.c;
 
-  // V^T operand (A of O^T += V^T P^T): lane l reads head_dim row 32*db + l%32, unit (ks, hl).
-  // (VPACK: region ks * D/32 + db, slot = lane.)
-  const int vt_base = VPACK ? lane * 16 : Vt<D>::off(l32, 0, hl, 0);
+  // V^T operand (A of O^T += V^T P^T): head_dim row 32*db + l%32 of the 32-row block, the 8 keys
+  // of k-step ks that lane half hl multiplies (16ks + 4hl + 0..3, then 16ks + 8 + 4hl + 0..3).
+  // VPACK: region ks * D/32 + db of the packed tile, slot = lane, one 128-bit read.  Otherwise
+  // two ds_read_b64_tr_b16 of the V rows: that instruction transposes 16-bit elements within
+  // each 16-lane group, lane j receiving element j%4 of the 8 bytes addressed by lane j/4 + 4t
+  // as its element t (t = 0..3).  Lane l (index i = l%16 in its group) therefore addresses key
+  // row 16ks + 4hl + i/4 (+8 for the second read), head_dim columns 32db + 16((l/16)%2) +
+  // 4(i%4) + 0..3, and receives keys 16ks + 4hl + 0..3 of column 32db + l%32.
+  const int vt_base = lane * 16;
+  const int tr_base = L::off(4 * hl + ((lane & 15) >> 2), (16 * ((lane >> 4) & 1) + 4 * (lane & 3)) >> 3) +
+                      8 * (lane & 1);
+  constexpr int TR_KS = (16 / RPR) * RS, TR_H = (8 / RPR) * RS, TR_DB = 4 * RPR * 16;
   auto v_operand = [&](const unsigned char* vb, int ks, int db) __attribute__((always_inline)) {
-    if constexpr (VPACK) return *(const u32x4*)(vb + vt_base + (ks * (D / 32) + db) * 1024);
-    else return *(const u32x4*)(vb + vt_base + ks * Vt<D>::KSS + db * Vt<D>::RGS);
+    if constexpr (VPACK) {
+      return *(const u32x4*)(vb + vt_base + (ks * (D / 32) + db) * 1024);
+    } else {
+      const int oa = tr_base + ks * TR_KS + db * TR_DB;
+      const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vb + oa));
+      const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vb + oa + TR_H));
+      const u32x2 lo2 = __builtin_bit_cast(u32x2, lo), hi2 = __builtin_bit_cast(u32x2, hi);
+      return (u32x4){lo2[0], lo2[1], hi2[0], hi2[1]};
+    }
   };
 
   // ---- Tile pipeline ("tile j" is the j-th tile of the walk: tix(j)).  Iteration j holds S_j
@@ -699,17 +718,16 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void fa_fwd_kernel(Params
   // instruction stream in which three independent pieces of work are interleaved:
   //   * S_{j+1} = K_{j+1} Q^T                 (matrix cores, K operands from LDS),
   //   * O += V_{j-1}^T P_{j-1}^T              (matrix cores, V^T operands from LDS, P in registers),
-  //   * the masked online softmax of S_j -> P_j, alpha_j, row sums (vector units),
-  // so every matrix instruction of the tile has vector work of the softmax beside it; then
-  // O *= alpha_j (skipped by a wave whose rows all kept their max) puts O on P_j's scale before
-  // the next iteration adds V_j^T P_j^T.  The iteration also issues the loads of the mask words
-  // of tile j+2 (registers, stored to LDS at its end), K_{j+2} (DMA into LDS) and V_j (DMA of
-  // the packed V^T tile, or the transposed write of V_j from registers loaded one iteration
-  // earlier, and the register load of V_{j+1}), and ends at the one workgroup barrier of the
-  // tile.  The keep words of tile j are carried in registers from iteration j-1, so the mask
-  // buffer of tile j can be refilled during iteration j.  After the last iteration one more
-  // V^T P^T product remains.  Loads past the last tile re-read the last tile (in bounds, never
-  // used).
+  //   * the masked online softmax of S_j -> P_j and its row sums (vector units),
+  // so every matrix instruction of the tile has vector work of the softmax beside it; then the
+  // sum check (softmax_finish), which in the rare case redoes the tile against its row max and
+  // rescales O before the next iteration adds V_j^T P_j^T.  The iteration also issues the loads
+  // of K_{j+2} and V_j (DMA into LDS) and of the mask words of tile j+3 (into a register; the
+  // words of tile j+2, loaded one iteration earlier, are stored to LDS at its end), and ends at
+  // the one workgroup barrier of the tile.  The keep words of tile j are carried in registers
+  // from iteration j-1, so the mask buffer of tile j can be refilled during iteration j.  After
+  // the last iteration one more V^T P^T product remains.  Loads past the last tile re-read the
+  // last tile (in bounds, never used).
 
   // The matrix instructions of one iteration, in one index space: i < NPV are O^T += V^T P^T
   // (k-step i / NDB, head_dim block i % NDB: k-step major, so each P register is dead after its
@@ -841,8 +859,7 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void fa_fwd_kernel(Params
   // Scheduling pattern of the interleaved stream, per part: each matrix instruction with the
   // operand read of a later one, a share of the tile's global loads and V^T writes (part a),
   // and VP vector instructions of the softmax (transcendentals included).
-  constexpr int NVMEM = (VPACK ? VDMA_PER_WAVE : (VS_THREADS == NT ? 4 : 0)) + DMA_PER_WAVE +
-                        (MODE == kBitmask ? 1 : 0);
+  constexpr int NVMEM = VDMA_PER_WAVE + DMA_PER_WAVE + (MODE == kBitmask ? 1 : 0);
   constexpr int VALU_A = 52 + (MODE == kBitmask ? 32 : 0);  // one block: mask, P, sums
   constexpr int VALU_B = VALU_A;
 #ifndef FA_VP_ADD
@@ -851,14 +868,17 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void fa_fwd_kernel(Params
   constexpr int VPA = (VALU_A + NPV - 1) / NPV + FA_VP_ADD, VPB = (VALU_B + NQK - 1) / NQK + FA_VP_ADD;
   auto stream_pattern = [&](int i0, int i1, auto vp, bool with_loads, bool first)
                             __attribute__((always_inline)) {
-    if (first) __builtin_amdgcn_sched_group_barrier(0x100, AH, 0);  // first operands
+    // (a V^T operand of the unpacked path is two reads)
+    if (first) __builtin_amdgcn_sched_group_barrier(0x100, VPACK ? AH : 2 * AH, 0);  // first operands
 #pragma unroll
     for (int i = 0; i < NMM; ++i) {
       if (i < i0 || i >= i1) continue;
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one matrix instruction
-      if (i + AH < NMM) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // a later operand
+      if (i + AH < NMM) {  // a later operand
+        if (!VPACK && i + AH < NPV) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        else __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
       if (with_loads && i - i0 < NVMEM) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-      if (with_loads && !VPACK && i - i0 < 8) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x402, decltype(vp)::value, 0);  // softmax (VALU, transcendental)
     }
   };
@@ -885,10 +905,8 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void fa_fwd_kernel(Params
     const int j0 = tix(j), j1 = tix(j + 1), j2 = tix(j + 2);
     auto issue_loads = [&]() __attribute__((always_inline)) {
       dma_tile(j2, k_fill);
-      v_dma(j0, v_fill);  // (VPACK) V_j^T straight into LDS
-      v_store(v_fill);    // V_j^T, from registers loaded during the previous iteration
+      v_dma(j0, v_fill);      // V_j (packed V^T, or rows) straight into LDS
       mask_load(tix(j + 3));  // (stays in flight past this iteration's wait)
-      v_load(j1);         // V_{j+1}: lands during this iteration, written in the next
     };
     Cls cls_nxt = classify(j1, m_nxt);
     const bool live_nxt = wave_live && j + 1 < n_tiles && !cls_nxt.skip;
@@ -934,13 +952,10 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void fa_fwd_kernel(Params
     softmax_finish(s_cur, pk);
 #pragma unroll
     for (int t = 0; t < PKS; ++t) pk_prev[t] = pk[t];
-    // This wave's K DMA and mask words have landed (the V loads, issued last, may still be in
-    // flight: they are consumed in the next iteration; on the packed path the V^T DMA has
-    // landed too).
-    // (issued last: the mask words of tile j+3, then the register loads of V_{j+1})
+    // This wave's K and V DMA and the mask words of tile j+2 have landed (the words of tile
+    // j+3, issued last, stay in flight).
     constexpr int MQ = MODE == kBitmask ? 1 : 0;
-    if (vs_thread) __builtin_amdgcn_s_waitcnt(waitcnt_imm(4 + MQ, 15));
-    else __builtin_amdgcn_s_waitcnt(waitcnt_imm(MQ, 15));
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm(MQ, 15));
     mask_store_queued(m_fill);  // the words of tile j+2, loaded during the previous iteration
     // This wave's LDS writes (mask words, V^T) are complete; then meet the other waves.
     __builtin_amdgcn_s_waitcnt(waitcnt_imm(63, 0));
@@ -956,17 +971,16 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void fa_fwd_kernel(Params
   u32x4 pk_prev[PKS];
 #pragma unroll
   for (int t = 0; t < PKS; ++t) pk_prev[t] = (u32x4){0u, 0u, 0u, 0u};
-  // Prologue: Q in registers; masks 0 and 1, K_0 and K_1 staged, V_0 in registers (register
-  // path); S_0 computed.  The Q loads of every staging pass go out first, then the K_0 / K_1
-  // DMA and the first V and mask loads, so all their latencies overlap the Q staging; the
-  // staging barriers wait only for the Q loads and LDS accesses (not for those DMAs).
+  // Prologue: Q in registers; masks 0 and 1, K_0 and K_1 staged; S_0 computed.  The Q loads of
+  // every staging pass go out first, then the K_0 / K_1 DMA and the first mask loads, so all
+  // their latencies overlap the Q staging; the staging barriers wait only for the Q loads and
+  // LDS accesses (not for those DMAs).
   {
     u32x4 qx[QPASS][QL];   // every pass's Q chunks loaded at once (one memory latency)
 #pragma unroll
     for (int pass = 0; pass < QPASS; ++pass) q_load(pass, qx[pass]);
     dma_tile(tix(0), k_lds0);
     dma_tile(tix(1), k_lds1);
-    v_load(tix(0));
     mask_load(tix(0));
 #pragma unroll
     for (int pass = 0; pass < QPASS; ++pass) {
@@ -1149,14 +1163,15 @@ hipError_t launch_merge(const Params& p, float* lse, hipStream_t s) {
                          args, 0, s);
 }
 
-// Instances: 4 waves with or without packed V, 8 waves with packed V (a KV head with that many
-// rows always has enough row tiles to pack V).
+// Instances: 4 or 8 waves, each with packed V^T or with V's rows.
 template <bool BF16, int D, int MODE>
 hipError_t launch(const Params& p, bool vpack, int nw, hipStream_t s) {
   void* args[] = {(void*)&p};
-  const void* k = nw == kWide ? (const void*)fa_fwd_kernel<BF16, D, MODE, true, kWide>
-                  : vpack     ? (const void*)fa_fwd_kernel<BF16, D, MODE, true, 4>
-                              : (const void*)fa_fwd_kernel<BF16, D, MODE, false, 4>;
+  if (vpack && !p.vt) return hipErrorInvalidValue;  // (the packed kernels read p.vt)
+  const void* k = nw == kWide ? (vpack ? (const void*)fa_fwd_kernel<BF16, D, MODE, true, kWide>
+                                       : (const void*)fa_fwd_kernel<BF16, D, MODE, false, kWide>)
+                              : (vpack ? (const void*)fa_fwd_kernel<BF16, D, MODE, true, 4>
+                                       : (const void*)fa_fwd_kernel<BF16, D, MODE, false, 4>);
   return hipLaunchKernel(k, dim3(p.n_wg), dim3(nw * 64), args, 0, s);
 }
 
@@ -1292,8 +1307,7 @@ fa_status make_plan(fa_dtype dtype, fa_mask_mode mask_mode, int batch, int n_q_h
   const int n_kt = (seq_len + kBN - 1) / kBN;
   const int64_t tile_bytes = head_dim == 128 ? VtPack<128>::TILE : VtPack<64>::TILE;
   const bool pack_ok = (int64_t)n_kt * tile_bytes < ((int64_t)1 << 31);
-  const int nw =
-      pack_ok && rows >= (mask_mode == FA_MASK_CAUSAL ? kWideRowsCausal : kWideRows) ? kWide : 4;
+  const int nw = rows >= (mask_mode == FA_MASK_CAUSAL ? kWideRowsCausal : kWideRows) ? kWide : 4;
   const int64_t n_rt = (rows + nw * 32 - 1) / (nw * 32);
   const int64_t n_wg = n_rt * n_kv_heads * batch;
   if (n_wg >= ((int64_t)1 << 31)) return FA_ERR_BAD_SHAPE;
@@ -1315,10 +1329,10 @@ fa_status make_plan(fa_dtype dtype, fa_mask_mode mask_mode, int batch, int n_q_h
                                         std::max<int64_t>(1, n_kt / 8)});
   }
   if (n_wg * n_split >= ((int64_t)1 << 31)) return FA_ERR_BAD_SHAPE;
-  // Packed V^T (one pre-pass over V) when each KV head's V tiles would otherwise be transposed
-  // by kPackRowTiles or more row-tile workgroups (always so for the 256-row workgroup).
+  // Packed V^T (one pre-pass over V) when kPackRowTiles or more row-tile workgroups would
+  // otherwise each transpose a KV head's V in their operand reads.
   pl->nw = nw;
-  pl->vpack = pack_ok && (nw == kWide || n_rt >= kPackRowTiles);
+  pl->vpack = pack_ok && n_rt >= kPackRowTiles;
   pl->n_split = n_split;
   pl->n_kt = n_kt;
   pl->n_rb = n_rb;

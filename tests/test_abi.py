@@ -147,9 +147,9 @@ def test_caller_workspace_checked_before_launch(kw):
 
 def test_plan_workspace_layout_with_split_and_packed_v():
     # packed V^T first, then the split-KV partials at the next 256-byte boundary
-    p = _plan(B=1, Hq=16, Hkv=16, S=1100, splits=2)
-    vt = 16 * 18 * 64 * 128 * 2
-    part = 2 * 1100 * 16 * (128 + 2) * 4
+    p = _plan(B=1, Hq=16, Hkv=16, S=8200, splits=2)
+    vt = 16 * 129 * 64 * 128 * 2
+    part = 2 * 8200 * 16 * (128 + 2) * 4
     assert p["packed_v"] == 1 and p["kv_splits"] == 2
     assert p["workspace_bytes"] == ((vt + 255) // 256) * 256 + part
 
@@ -236,13 +236,26 @@ def test_plan_row_thresholds():
 
 
 def test_plan_short_masked():
-    # S = 512: four 128-row tiles per head, V transposed in-kernel, nothing allocated
+    # S = 512 and 1000: four and eight 128-row tiles per head, V's rows read by each workgroup,
+    # nothing allocated
     p = _plan(dtype=F16, mode=BITMASK, B=16, S=512, D=64)
     assert p == {"rows_per_workgroup": 128, "packed_v": 0, "kv_splits": 1, "kernels": 1,
                  "workgroups": 16 * 16 * 4, "workspace_bytes": 0}
-    # S = 1000: eight row tiles per head -> V packed once per call (16 tiles x 8 KiB per head)
     p = _plan(dtype=F16, mode=BITMASK, B=16, S=1000, D=64)
-    assert p["packed_v"] == 1 and p["workspace_bytes"] == 16 * 16 * 16 * 64 * 64 * 2
+    assert p["packed_v"] == 0 and p["workspace_bytes"] == 0 and p["kernels"] == 1
+
+
+@pytest.mark.parametrize("mode,rows,nw_rows,packed", [
+    (NONE, 3968, 128, 0), (NONE, 3969, 128, 1), (NONE, 4096, 256, 0), (NONE, 7936, 256, 0),
+    (NONE, 7937, 256, 1), (BITMASK, 4095, 128, 1), (BITMASK, 7937, 256, 1),
+    (CAUSAL, 3968, 128, 0), (CAUSAL, 3969, 128, 1), (CAUSAL, 8191, 128, 1), (CAUSAL, 8192, 256, 1),
+])
+def test_plan_packs_v_from_32_row_tiles(mode, rows, nw_rows, packed):
+    # V is packed once per call when a KV head's rows make 32 or more row tiles; otherwise each
+    # workgroup reads V's rows (no workspace).  One head: rows per KV head = S.
+    p = _plan(mode=mode, dtype=F16, D=64, B=1, Hq=1, Hkv=1, S=rows)
+    assert p["rows_per_workgroup"] == nw_rows and p["packed_v"] == packed
+    assert (p["workspace_bytes"] > 0) == bool(packed) and p["kernels"] == 1 + packed
 
 
 def test_plan_split_kv():

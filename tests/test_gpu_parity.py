@@ -116,8 +116,11 @@ def test_causal_few_heads_split_over_xcds(B, S, Hq, Hkv):
 
 
 @pytest.mark.parametrize("S,Hq,Hkv,mode,D,dtype", [
-    (1500, 4, 4, "none", 128, "bf16"),      # 1500 rows per KV head: 128-row tiles, packed V
-    (1100, 16, 2, "none", 128, "bf16"),     # 8800 rows: 256-row workgroups
+    (1500, 4, 4, "none", 128, "bf16"),      # 1500 rows per KV head: 128-row tiles, V's rows
+    (4500, 2, 2, "causal", 64, "f16"),      # 4500 rows: 128-row tiles, packed V
+    (700, 8, 1, "none", 128, "bf16"),       # 5600 rows: 256-row workgroups, V's rows
+    (600, 8, 1, "bitmask", 64, "f16"),      # 4800 rows: 256-row workgroups, V's rows
+    (1100, 16, 2, "none", 128, "bf16"),     # 8800 rows: 256-row workgroups, packed V
     (2100, 16, 2, "causal", 128, "bf16"),   # 16800 rows: 256-row workgroups, causal
     (1030, 8, 1, "bitmask", 64, "f16"),     # 8240 rows: 256-row workgroups, bitmask
     (1030, 8, 1, "bitmask", 128, "bf16"),
@@ -216,11 +219,12 @@ def test_no_out_of_bounds_writes(S):
 # end, so each row's running maximum rises past the kernel's slack many times along the
 # sequence and the rescale of O and of the row sum runs repeatedly, on every workgroup shape.
 @pytest.mark.parametrize("mode,D,dtype,B,S,Hq,Hkv,full", [
-    ("none", 128, "bf16", 1, 4096, 2, 2, False),     # 256-row workgroups, packed V^T
-    ("causal", 128, "bf16", 1, 8192, 1, 1, False),   # 256-row causal workgroups
+    ("none", 128, "bf16", 1, 4096, 2, 2, False),     # 256-row workgroups, V's rows
+    ("causal", 128, "bf16", 1, 8192, 1, 1, False),   # 256-row causal workgroups, packed V^T
     ("none", 128, "bf16", 1, 1024, 8, 2, True),      # GQA group of 4, 256-row workgroups
-    ("causal", 128, "bf16", 2, 700, 4, 4, True),     # 128-row workgroups, V^T in-kernel
-    ("bitmask", 64, "f16", 2, 1000, 2, 2, True),     # 128-row workgroups, packed V^T
+    ("causal", 128, "bf16", 2, 700, 4, 4, True),     # 128-row workgroups, V's rows
+    ("bitmask", 64, "f16", 2, 1000, 2, 2, True),     # 128-row workgroups, V's rows
+    ("causal", 64, "f16", 1, 4500, 2, 2, False),     # 128-row workgroups, packed V^T
     ("bitmask", 128, "f16", 1, 300, 3, 1, True),     # GQA group of 3, ragged tail
     ("none", 64, "f16", 1, 333, 2, 1, True),
 ], ids=lambda x: str(x))

@@ -22,9 +22,9 @@ def _inputs(B, S, Hq, Hkv, D, dtype, mode, seed):
 
 @pytest.mark.parametrize("mode", ["none", "causal", "bitmask"])
 def test_side_stream_matches_default_stream(mode):
-    # 2048 positions x 4 heads: 16 row tiles per KV head, so V is packed by the pre-pass into a
-    # workspace from the pool; split-KV takes its partials from the same pool.
-    w, q, k, v, m = _inputs(1, 2048, 4, 4, 128, "bf16", mode, seed=21000)
+    # 8192 positions x 2 heads: 32 or 64 row tiles per KV head, so V is packed by the pre-pass
+    # into a workspace from the pool; split-KV takes its partials from the same pool.
+    w, q, k, v, m = _inputs(1, 8192, 2, 2, 128, "bf16", mode, seed=21000)
     log(f"case side stream {mode}")
     o_ref = fa_fwd(q, k, v, mode=mode, scale=w.scale, mask=m)
     o_ref_split = fa_fwd(q, k, v, mode=mode, scale=w.scale, mask=m, kv_splits=3)
@@ -46,7 +46,7 @@ def test_two_streams_at_once():
     # Two calls with different inputs and shapes in flight together on two streams, each with
     # its own packed-V workspace, then each checked bitwise against the same call made alone.
     a = _inputs(2, 4096, 8, 2, 128, "bf16", "none", seed=21100)
-    b = _inputs(1, 3000, 4, 4, 64, "f16", "causal", seed=21200)
+    b = _inputs(1, 4096, 4, 4, 64, "f16", "causal", seed=21200)
     log("case two streams at once")
     ref = []
     for w, q, k, v, m in (a, b):

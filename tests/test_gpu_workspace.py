@@ -12,8 +12,8 @@ DEV = torch.device("cuda:0")
 
 
 @pytest.mark.parametrize("B,S,Hq,Hkv,D,mode,splits", [
-    (1, 4096, 16, 16, 128, "none", 1),      # packed V (256-row workgroups)
-    (2, 1000, 16, 16, 64, "bitmask", 1),    # packed V (128-row workgroups, d64)
+    (1, 8192, 16, 16, 128, "none", 1),      # packed V (256-row workgroups)
+    (1, 4000, 4, 4, 64, "bitmask", 1),      # packed V (128-row workgroups, d64)
     (1, 4096, 1, 1, 128, "causal", 0),      # automatic split-KV: packed V + partials
     (1, 1100, 16, 2, 128, "none", 3),       # explicit split
 ])
@@ -49,9 +49,10 @@ def test_workspace_not_needed_is_ignored():
 
 def test_workspace_too_small_rejected():
     from attention_forward_fwd_amd import FaError
-    w = inputs.mha_prefill(1, 4096, False)
+    w = inputs.mha_prefill(1, 8192, False)   # packed V: a workspace is needed
     q, k, v = (t.to(DEV) for t in inputs.make_qkv_device(w, DEV))
     need = workspace_bytes(q, k, "none")
+    assert need > 256
     o = torch.full_like(q, 7.0)
     with pytest.raises(FaError) as ei:
         fa_fwd(q, k, v, out=o, workspace=torch.empty(need - 256, dtype=torch.uint8, device=DEV))
