@@ -804,28 +804,61 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void fa_fwd_kernel(Params
   // function of (m, l) whatever m is.  An all -inf tile gives P = 0 and leaves m and l alone.
   constexpr float kSumBound = 32768.f;  // 2^15
   float ps_sm[2];
-  auto exp_block = [&](f32x16 (&s)[NKB], u32x4 (&pk)[PKS], int kb32) __attribute__((always_inline)) {
+  // Bitmask mode applies the keep bits to the packed weights (masked = true, w = the block's
+  // pre-shifted keep word): a register of P holds two consecutive keys of the lane, bits b and
+  // b+1 of w for the block's first 16 keys (b = 0, 2, 8, 10) and b+16, b+17 for the last 16.
+  // w << (15 - k) puts bit k at bit 15 and bit k+16 at bit 31, the bits v_perm_b32's selectors
+  // 8..11 replicate into a byte, so one permute of two such words gives a register's mask
+  // (0xffff per kept half): 1.5 vector instructions per key instead of the 2 of mask_block.
+  // The weights of masked keys are computed and then cleared (an infinite one included; s is
+  // finite), and the row sums add the cleared values.
+  auto exp_block = [&](f32x16 (&s)[NKB], u32x4 (&pk)[PKS], int kb32, auto masked, u32 w)
+                       __attribute__((always_inline)) {
+    constexpr bool MASKED = decltype(masked)::value;
+    u32 a[8];
+    if constexpr (MASKED) {
+      constexpr int kq[8] = {0, 1, 2, 3, 8, 9, 10, 11};
+#pragma unroll
+      for (int q = 0; q < 8; ++q) a[q] = w << (15 - kq[q]);
+    }
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       f32x8 t;
 #pragma unroll
       for (int e = 0; e < 8; ++e) t[e] = __builtin_amdgcn_exp2f(fmaf(s[kb32][8 * h + e], c, -m_run));
-      const u32x4 pw = pack8<BF16>(t);
+      u32x4 pw = pack8<BF16>(t);
+      if constexpr (MASKED) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int q0 = 2 * (e & 1) + 4 * (e >> 1);
+          pw[e] &= __builtin_amdgcn_perm(a[q0 + 1], a[q0], h ? 0x0B0B0909u : 0x0A0A0808u);
+        }
+      }
       pk[2 * kb32 + h] = pw;
 #pragma unroll
       for (int e = 0; e < 4; ++e) ps_sm[e & 1] = dot2_ones<BF16>(pw[e], ps_sm[e & 1]);
     }
   };
+#ifndef FA_PAIR_MASK
+#define FA_PAIR_MASK 1
+#endif
+  constexpr bool PAIR_MASK = MODE == kBitmask && FA_PAIR_MASK;
   auto softmax_block = [&](const Cls& cls, f32x16 (&s)[NKB], u32x4 (&pk)[PKS], int kb32)
                            __attribute__((always_inline)) {
     if (kb32 == 0) ps_sm[0] = ps_sm[1] = 0.f;
-    if (MODE == kBitmask) mask_block(cls, s, kb32);
-    exp_block(s, pk, kb32);
+    if constexpr (PAIR_MASK) {
+      exp_block(s, pk, kb32, std::true_type{}, cls.wsh[kb32]);
+    } else {
+      if (MODE == kBitmask) mask_block(cls, s, kb32);
+      exp_block(s, pk, kb32, std::false_type{}, 0u);
+    }
   };
-  auto softmax_finish = [&](f32x16 (&s)[NKB], u32x4 (&pk)[PKS]) __attribute__((always_inline)) {
+  auto softmax_finish = [&](const Cls& cls, f32x16 (&s)[NKB], u32x4 (&pk)[PKS]) __attribute__((always_inline)) {
     float ps = ps_sm[0] + ps_sm[1];
     float alpha = 1.f;
     if (__builtin_amdgcn_ballot_w64(!(ps <= kSumBound))) {  // (a NaN or infinite sum included)
+      // (the weights were masked after the exp: mask the scores themselves for the row max)
+      if constexpr (PAIR_MASK) mask_scores(cls, s);
       // Row max: two in-lane chains of 3-input maxima (v_max3_f32), one per 32-key block, then
       // across the two lane halves; the max moves straight to the tile's max.
       float mx2[NKB];
@@ -844,7 +877,7 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void fa_fwd_kernel(Params
       m_run = m_new;
       ps_sm[0] = ps_sm[1] = 0.f;
 #pragma unroll
-      for (int kb32 = 0; kb32 < NKB; ++kb32) exp_block(s, pk, kb32);
+      for (int kb32 = 0; kb32 < NKB; ++kb32) exp_block(s, pk, kb32, std::false_type{}, 0u);
       ps = ps_sm[0] + ps_sm[1];
       // O (all tiles before this one) onto the new max before this tile's V^T P^T is added;
       // every lane multiplies (no per-lane branch).
@@ -860,7 +893,7 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void fa_fwd_kernel(Params
   // operand read of a later one, a share of the tile's global loads and V^T writes (part a),
   // and VP vector instructions of the softmax (transcendentals included).
   constexpr int NVMEM = VDMA_PER_WAVE + DMA_PER_WAVE + (MODE == kBitmask ? 1 : 0);
-  constexpr int VALU_A = 52 + (MODE == kBitmask ? 32 : 0);  // one block: mask, P, sums
+  constexpr int VALU_A = 52 + (MODE == kBitmask ? (PAIR_MASK ? 24 : 32) : 0);  // one block: mask, P, sums
   constexpr int VALU_B = VALU_A;
 #ifndef FA_VP_ADD
 #define FA_VP_ADD 0
@@ -949,7 +982,7 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void fa_fwd_kernel(Params
       softmax_block(cls_cur, s_cur, pk, 1);
     }
     __builtin_amdgcn_sched_barrier(0);
-    softmax_finish(s_cur, pk);
+    softmax_finish(cls_cur, s_cur, pk);
 #pragma unroll
     for (int t = 0; t < PKS; ++t) pk_prev[t] = pk[t];
     // This wave's K and V DMA and the mask words of tile j+2 have landed (the words of tile
