@@ -935,11 +935,15 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void fa_fwd_kernel(Params
                   const unsigned char* k_nxt, unsigned char* k_fill, const unsigned char* v_prev,
                   unsigned char* v_fill, const u32* m_nxt, u32* m_fill)
                   __attribute__((always_inline)) {
-    const int j0 = tix(j), j1 = tix(j + 1), j2 = tix(j + 2);
+    // (the branch-free loop never walks a tile summary: its tile j is kt0 + j)
+    auto tx = [&](int jj) __attribute__((always_inline)) {
+      return decltype(skip)::value ? tix(jj) : kt0 + min(jj, n_tiles - 1);
+    };
+    const int j0 = tx(j), j1 = tx(j + 1), j2 = tx(j + 2);
     auto issue_loads = [&]() __attribute__((always_inline)) {
       dma_tile(j2, k_fill);
       v_dma(j0, v_fill);      // V_j (packed V^T, or rows) straight into LDS
-      mask_load(tix(j + 3));  // (stays in flight past this iteration's wait)
+      mask_load(tx(j + 3));   // (stays in flight past this iteration's wait)
     };
     Cls cls_nxt = classify(j1, m_nxt);
     const bool live_nxt = wave_live && j + 1 < n_tiles && !cls_nxt.skip;
