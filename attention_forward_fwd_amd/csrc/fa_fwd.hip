@@ -636,9 +636,6 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void fa_fwd_kernel(Params
       mvalid = mrow_ok && word < p.W;
     }
   };
-  auto mask_store = [&](u32* mb) __attribute__((always_inline)) {
-    if (MODE == kBitmask) mb[m_row * NKB + m_word] = mvalid ? mreg : 0u;
-  };
   auto mask_store_queued = [&](u32* mb) __attribute__((always_inline)) {
     if (MODE == kBitmask) {
       mb[m_row * NKB + m_word] = mq_valid ? mq : 0u;
@@ -1012,13 +1009,22 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void fa_fwd_kernel(Params
   // every staging pass go out first, then the K_0 / K_1 DMA and the first mask loads, so all
   // their latencies overlap the Q staging; the staging barriers wait only for the Q loads and
   // LDS accesses (not for those DMAs).
+  u32 mw0 = 0u, mw1 = 0u;  // mask words of tiles 0 and 1 (bitmask mode)
+  bool mv0 = false, mv1 = false;
   {
     u32x4 qx[QPASS][QL];   // every pass's Q chunks loaded at once (one memory latency)
 #pragma unroll
     for (int pass = 0; pass < QPASS; ++pass) q_load(pass, qx[pass]);
     dma_tile(tix(0), k_lds0);
     dma_tile(tix(1), k_lds1);
+    // The mask words of tiles 0, 1 and 2 go out together (one memory latency for the three).
     mask_load(tix(0));
+    mw0 = mreg;
+    mv0 = mvalid;
+    mask_load(tix(1));
+    mw1 = mreg;
+    mv1 = mvalid;
+    mask_load(tix(2));  // (queued: stored at the end of iteration 0)
 #pragma unroll
     for (int pass = 0; pass < QPASS; ++pass) {
       // (Buffer choices are static, so the compiler can tell these LDS accesses from the DMA
@@ -1054,12 +1060,11 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void fa_fwd_kernel(Params
     const int c = tid + NT * i;
     if (c < VBUF_BYTES / 16) *(u32x4*)(v_lds1 + 16 * c) = (u32x4){0u, 0u, 0u, 0u};
   }
-  __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 15));  // K_0, K_1 DMA and the mask words of tile 0
-  mask_store(m_lds0);
-  mask_load(tix(1));
-  __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 15));
-  mask_store(m_lds1);
-  mask_load(tix(2));  // (queued: stored at the end of iteration 0)
+  __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 15));  // K_0, K_1 DMA and the mask words
+  if (MODE == kBitmask) {
+    m_lds0[m_row * NKB + m_word] = mv0 ? mw0 : 0u;
+    m_lds1[m_row * NKB + m_word] = mv1 ? mw1 : 0u;
+  }
   mq = mreg;
   mq_valid = mvalid;
   __syncthreads();
