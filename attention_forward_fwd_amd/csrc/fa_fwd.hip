@@ -219,10 +219,11 @@ struct Lds {
   }
 };
 
-// LDS layout of a transposed V tile.  Row d (one head_dim index) holds the tile's BN = 64
-// keys as 8 "units" of 16 bytes: unit (ks, hl) holds keys 16ks + 4hl + 0..3 (first 8 bytes) and
-// 16ks + 8 + 4hl + 0..3 (last 8 bytes), exactly the 8 keys, in register order, that lane half hl
-// of an MFMA needs at k-step ks of P V, so each V^T operand is one 128-bit read.  Units of one
+// LDS layout of a transposed V tile in the packing pre-pass.  Row d (one head_dim index) holds
+// the tile's BN = 64 keys as 8 "units" of 16 bytes: unit (ks, hl) holds keys 16ks + 4hl + 0..3
+// (first 8 bytes) and 16ks + 8 + 4hl + 0..3 (last 8 bytes), exactly the 8 keys, in register
+// order, that lane half hl of an MFMA needs at k-step ks of P V (the packed tile keeps the
+// units, so each V^T operand of the attention kernel is one 128-bit read).  Units of one
 // k-step and one 32-row block of d form a 1 KiB region (4 lines of 8 rows x 2 units), padded
 // to RGS bytes; within a line, unit hl of row d sits at 16-byte slot
 // (2 (d % 8) + hl) ^ ((d / 8) % 4) ^ x(hl).  With 64 banks x 4 B:
