@@ -157,6 +157,27 @@ def test_padding_bits_ignored():
     assert torch.equal(a, b), "bits for keys >= S changed the output"
 
 
+@pytest.mark.parametrize("D,dtype", [(64, "f16"), (128, "bf16")])
+def test_masked_keys_with_huge_scores(D, dtype):
+    # Bitmask mode forms every key's weight and clears the masked ones afterwards.  Here some keys
+    # are scaled up so far that their weights overflow (to infinity in fp32, and in fp16 / bf16)
+    # against the running max, and every row masks them out: they must contribute exactly
+    # nothing, the kept keys must still give the oracle's result, and no NaN may appear.
+    S, H = 700, 2
+    q, k, v = _qkv(1, S, H, H, D, dtype, 9250 + D)
+    huge = torch.arange(S) % 37 == 5                      # every 37th key, from key 5
+    k = k.clone()
+    k[0, huge] = (k[0, huge].float() * 400.0).to(k.dtype)  # scores of hundreds of exp2 units
+    words = _mask(1, H, S, 9251 + D).numpy().view(np.uint32).copy()
+    for j in np.nonzero(huge.numpy())[0]:
+        words[..., j // 32] &= ~np.uint32(1 << (j % 32))  # masked for every row
+    m = torch.from_numpy(words.view(np.int32))
+    label = f"huge masked scores d{D} {dtype}"
+    log(f"case {label}")
+    _, o = check_full(q, k, v, "bitmask", D ** -0.5, m, label)
+    assert bool(torch.isfinite(o).all())
+
+
 def test_single_kept_key_returns_value_row():
     S, H, D = 150, 2, 128
     q, k, v = _qkv(1, S, H, H, D, "bf16", 9200)
