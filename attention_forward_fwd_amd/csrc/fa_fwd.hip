@@ -933,9 +933,12 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void fa_fwd_kernel(Params
                   const unsigned char* k_nxt, unsigned char* k_fill, const unsigned char* v_prev,
                   unsigned char* v_fill, const u32* m_nxt, u32* m_fill)
                   __attribute__((always_inline)) {
-    // (the branch-free loop never walks a tile summary: its tile j is kt0 + j)
+    // skip: 0 = branch-free, 1 = skipping (a wave with both neighbouring tiles dead does no
+    // matrix work), 2 = the first iteration of the branch-free loop (no P_{-1}: part a has no
+    // matrix work).  (The branch-free loop never walks a tile summary: its tile j is kt0 + j.)
+    constexpr int KIND = decltype(skip)::value;
     auto tx = [&](int jj) __attribute__((always_inline)) {
-      return decltype(skip)::value ? tix(jj) : kt0 + min(jj, n_tiles - 1);
+      return KIND == 1 ? tix(jj) : kt0 + min(jj, n_tiles - 1);
     };
     const int j0 = tx(j), j1 = tx(j + 1), j2 = tx(j + 2);
     auto issue_loads = [&]() __attribute__((always_inline)) {
@@ -953,7 +956,15 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void fa_fwd_kernel(Params
 #ifdef FA_PRIO_A
     __builtin_amdgcn_s_setprio(FA_PRIO_A);
 #endif
-    if (!decltype(skip)::value || live_nxt || live_prev) {
+    if constexpr (KIND == 2) {
+      issue_loads();
+      mm_prefetch(NPV, NMM, op, k_nxt, v_prev);
+      softmax_block(cls_cur, s_cur, pk, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      mm_run(NPV, NMM, NMM, op, k_nxt, s_nxt, v_prev, pk_prev);
+      softmax_block(cls_cur, s_cur, pk, 1);
+      stream_pattern(NPV, NMM, std::integral_constant<int, VPB>{}, true, true);
+    } else if (KIND == 0 || live_nxt || live_prev) {
       issue_loads();  // (in the stream's scheduling region, spread over its first instructions)
       // One interleaved stream in two parts.  Both products run: when one of the two tiles is
       // skipped, its P is exactly 0 (so O += V^T P^T adds zeros; V^T in LDS is always finite
@@ -1088,13 +1099,35 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void fa_fwd_kernel(Params
   if (MODE == kCausal) n_fast = min(n_tiles, min((row0 + 31) / G, S - 1) / BN);
   if (sparse) n_fast = 0;
   n_fast &= ~1;
-  const std::integral_constant<bool, false> fast{};
-  const std::integral_constant<bool, true> skipping{};
-  for (int j = 0; j < n_fast; j += 2) {
-    iter(fast, j, cls_cur, live_cur, live_prev, sA, sB, pk_prev, k_lds1, k_lds0, v_lds1, v_lds0,
+  const std::integral_constant<int, 0> fast{};
+  const std::integral_constant<int, 1> skipping{};
+  const std::integral_constant<int, 2> first{};
+#ifndef FA_PEEL
+#define FA_PEEL 1
+#endif
+  // With a bit mask the extra copy of the iteration's code measured slower than the product it
+  // saves, so only the other modes peel iteration 0.
+  constexpr bool kPeel = FA_PEEL && MODE != kBitmask;
+  if (kPeel && n_fast >= 2) {
+    // Iteration 0 without the product of P_{-1} = 0, then pairs from iteration 1, then the last
+    // branch-free iteration (n_fast is even).
+    iter(first, 0, cls_cur, live_cur, live_prev, sA, sB, pk_prev, k_lds1, k_lds0, v_lds1, v_lds0,
          m_lds1, m_lds0);
-    iter(fast, j + 1, cls_cur, live_cur, live_prev, sB, sA, pk_prev, k_lds0, k_lds1, v_lds0,
+    for (int j = 1; j + 1 < n_fast; j += 2) {
+      iter(fast, j, cls_cur, live_cur, live_prev, sB, sA, pk_prev, k_lds0, k_lds1, v_lds0, v_lds1,
+           m_lds0, m_lds1);
+      iter(fast, j + 1, cls_cur, live_cur, live_prev, sA, sB, pk_prev, k_lds1, k_lds0, v_lds1,
+           v_lds0, m_lds1, m_lds0);
+    }
+    iter(fast, n_fast - 1, cls_cur, live_cur, live_prev, sB, sA, pk_prev, k_lds0, k_lds1, v_lds0,
          v_lds1, m_lds0, m_lds1);
+  } else {
+    for (int j = 0; j < n_fast; j += 2) {
+      iter(fast, j, cls_cur, live_cur, live_prev, sA, sB, pk_prev, k_lds1, k_lds0, v_lds1, v_lds0,
+           m_lds1, m_lds0);
+      iter(fast, j + 1, cls_cur, live_cur, live_prev, sB, sA, pk_prev, k_lds0, k_lds1, v_lds0,
+           v_lds1, m_lds0, m_lds1);
+    }
   }
   for (int j = n_fast; j < n_tiles; j += 2) {
     iter(skipping, j, cls_cur, live_cur, live_prev, sA, sB, pk_prev, k_lds1, k_lds0, v_lds1,
