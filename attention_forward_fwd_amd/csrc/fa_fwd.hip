@@ -1144,7 +1144,7 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void fa_fwd_kernel(Params
     mm_run(0, NPV, NPV, op, k_lds0, sA, vb, pk_prev);
   }
 
-  // ---- Epilogue: O / l (0 for a row with no kept key), rounded, 8-byte stores.
+  // ---- Epilogue: O / l (0 for a row with no kept key), rounded, stored row-major through LDS.
   const float lt = sum_halves(l_run);
   if (p.n_split > 1) {  // split-KV: this key range's unnormalised O, running max and row sum
     if (wave_live && my_pos < S) {
@@ -1164,7 +1164,44 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void fa_fwd_kernel(Params
     return;
   }
   const float inv = lt > 0.f ? __builtin_amdgcn_rcpf(lt) : 0.f;
-  if (wave_live && my_pos < S) {
+#ifndef FA_OSTAGE
+#define FA_OSTAGE 1
+#endif
+  if constexpr (FA_OSTAGE) {
+    // O rows through LDS.  A lane holds 8-byte pieces of its own row, so storing from registers
+    // writes 16 bytes of each of 32 rows per instruction; instead each wave writes its rows, one
+    // half of the columns at a time (OW bytes a row, rows OW + 8 bytes apart), into a region of
+    // its own in the K buffers (no wave reads them once the key loop has ended), reads them
+    // back row-major, 16 bytes a lane, and stores whole row halves: 128-byte lines at d=128.
+    // (A wave's LDS accesses complete in order, so no barrier is needed around its region.)
+    constexpr int OW = D;               // bytes of one half of a row
+    constexpr int ORS = OW + 8;         // row stride of a region
+    constexpr int OLR = OW / 16;        // lanes per row half
+    constexpr int ORI = 64 / OLR;       // rows per store instruction
+    static_assert((NW / 2) * 32 * ORS <= T_BYTES, "O staging regions fit the K buffers");
+    if (wave_live) {
+      unsigned char* ost = (wave < NW / 2 ? k_lds0 : k_lds1) + (wave % (NW / 2)) * (32 * ORS);
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+#pragma unroll
+        for (int dbl = 0; dbl < NDB / 2; ++dbl)
+#pragma unroll
+          for (int t4 = 0; t4 < 4; ++t4) {
+            f32x4 x;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) x[e] = oacc[h * (NDB / 2) + dbl][4 * t4 + e] * inv;
+            *(u32x2*)(ost + l32 * ORS + (32 * dbl + 8 * t4 + 4 * hl) * 2) = pack4<BF16>(x);
+          }
+#pragma unroll
+        for (int i = 0; i < 32 / ORI; ++i) {
+          const int r = lane / OLR + ORI * i, c = lane % OLR;
+          const u32x4 x = *(const u32x4*)(ost + r * ORS + 16 * c);
+          const int grow = row0 + wave * 32 + r, pos = grow / G, head = hk * G + (grow - pos * G);
+          if (pos < S) *(u32x4*)(p.o + q_batch + ((size_t)pos * Hq + head) * D + h * (D / 2) + 8 * c) = x;
+        }
+      }
+    }
+  } else if (wave_live && my_pos < S) {
     uint16_t* orow = p.o + q_batch + ((size_t)my_pos * Hq + my_head) * D;
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
@@ -1175,6 +1212,8 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void fa_fwd_kernel(Params
         for (int e = 0; e < 4; ++e) x[e] = oacc[db][4 * t4 + e] * inv;
         *(u32x2*)(orow + 32 * db + 8 * t4 + 4 * hl) = pack4<BF16>(x);
       }
+  }
+  if (wave_live && my_pos < S) {
     // Log-sum-exp of the row's kept scores (natural log), from the running softmax state: the
     // max m_run is of s*c with c = |scale| log2(e) (Q carries the sign of the scale), and lt
     // is the sum of 2^(s*c - m_run), so ln(sum exp(scale s)) = (m_run + log2 lt) ln 2.  A row
