@@ -123,6 +123,7 @@ def test_causal_few_heads_split_over_xcds(B, S, Hq, Hkv):
     (1100, 16, 2, "none", 128, "bf16"),     # 8800 rows: 256-row workgroups, packed V
     (2100, 16, 2, "causal", 128, "bf16"),   # 16800 rows: 256-row workgroups, causal
     (1030, 8, 1, "bitmask", 64, "f16"),     # 8240 rows: 256-row workgroups, bitmask
+    (1024, 8, 1, "bitmask", 64, "f16"),     # 8192 rows: 256-row workgroups, packed V, bitmask
     (1030, 8, 1, "bitmask", 128, "bf16"),
 ])
 def test_workgroup_shapes_ragged(S, Hq, Hkv, mode, D, dtype):
