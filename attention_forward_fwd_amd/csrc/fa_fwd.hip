@@ -123,7 +123,11 @@ constexpr int kWide = 8;          // waves of the 256-row workgroup
 #define FA_WIDE_ROWS_CAUSAL 8192
 #endif
 constexpr int kWideRows = FA_WIDE_ROWS;   // rows per KV head (S x G) from which it is used
-constexpr int kWideRowsCausal = FA_WIDE_ROWS_CAUSAL;   // (causal: its longer diagonal tail favours 128 rows below)
+constexpr int kWideRowsCausal = FA_WIDE_ROWS_CAUSAL;   // (causal at d=64: its short tiles favour 128 rows below)
+#ifndef FA_WIDE_ROWS_CAUSAL_D128
+#define FA_WIDE_ROWS_CAUSAL_D128 4096
+#endif
+constexpr int kWideRowsCausal128 = FA_WIDE_ROWS_CAUSAL_D128;  // causal at d=128
 // Row tiles per KV head from which V is packed once per call (below it, each workgroup reads V's
 // rows through transposing LDS reads: the pre-pass costs more than those reads save).
 #ifndef FA_PACK_ROW_TILES
@@ -1438,7 +1442,9 @@ fa_status make_plan(fa_dtype dtype, fa_mask_mode mask_mode, int batch, int n_q_h
   const int n_kt = (seq_len + kBN - 1) / kBN;
   const int64_t tile_bytes = head_dim == 128 ? VtPack<128>::TILE : VtPack<64>::TILE;
   const bool pack_ok = (int64_t)n_kt * tile_bytes < ((int64_t)1 << 31);
-  const int nw = rows >= (mask_mode == FA_MASK_CAUSAL ? kWideRowsCausal : kWideRows) ? kWide : 4;
+  const int64_t wide_rows = mask_mode != FA_MASK_CAUSAL ? kWideRows
+                            : head_dim == 128 ? kWideRowsCausal128 : kWideRowsCausal;
+  const int nw = rows >= wide_rows ? kWide : 4;
   const int64_t n_rt = (rows + nw * 32 - 1) / (nw * 32);
   const int64_t n_wg = n_rt * n_kv_heads * batch;
   if (n_wg >= ((int64_t)1 << 31)) return FA_ERR_BAD_SHAPE;

@@ -227,9 +227,12 @@ def test_plan_prefill_uses_256_row_workgroups_and_packed_v():
 
 
 def test_plan_row_thresholds():
-    # 256-row workgroups from 4096 rows per KV head (S x G), 8192 for causal
+    # 256-row workgroups from 4096 rows per KV head (S x G), 8192 for causal at head_dim 64
     assert _plan(B=8, S=4096)["rows_per_workgroup"] == 256
-    assert _plan(B=8, S=4096, mode=CAUSAL)["rows_per_workgroup"] == 128
+    assert _plan(B=8, S=4096, mode=CAUSAL)["rows_per_workgroup"] == 256
+    assert _plan(B=8, S=4095, mode=CAUSAL)["rows_per_workgroup"] == 128
+    assert _plan(B=2, S=4096, mode=CAUSAL, D=64, dtype=F16)["rows_per_workgroup"] == 128
+    assert _plan(B=2, S=8192, mode=CAUSAL, D=64, dtype=F16)["rows_per_workgroup"] == 256
     assert _plan(B=4, S=8192, mode=CAUSAL)["rows_per_workgroup"] == 256
     assert _plan(B=16, S=2048)["rows_per_workgroup"] == 128
     assert _plan(B=16, S=2048, Hq=32, Hkv=8)["rows_per_workgroup"] == 256   # 2048 x 4 rows
