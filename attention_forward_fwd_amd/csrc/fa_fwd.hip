@@ -634,14 +634,15 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void fa_fwd_kernel(Params
   // words per row, so the BM x NKB words of a tile take one load per thread).  The row pointer
   // is clamped to a valid row and the word index to the row length, so the load needs no
   // branch; words of rows >= S or past the row end are then replaced by 0.  A tile's words are
-  // loaded three tiles ahead into a register and stored to LDS one iteration later, so each
-  // load (from HBM: every word is read once) has two iterations to arrive.
+  // loaded into a register at the end of the iteration two before the one that stores them to
+  // LDS, after that iteration's wait for all of its loads: the load (from HBM: every word is
+  // read once) then has a whole iteration to arrive, and it is the only vector load a wave has
+  // in flight at the barrier, so no wait ever depends on the order in which the compiler issues
+  // the tile's loads.
   static_assert(MODE != kBitmask || BM * NKB == NT, "one mask word per thread and tile");
   u32 mreg = 0u;        // the word most recently loaded ...
   bool mvalid = false;  // ... and whether it is a real word of a valid row (applied at the store,
                         // so no wait for the load is forced where it is issued)
-  u32 mq = 0u;          // the word loaded one iteration earlier (the next one to store)
-  bool mq_valid = false;
   const u32* mrow = nullptr;
   bool mrow_ok = false;
   const int m_row = tid % BM, m_word = tid / BM;
@@ -657,12 +658,8 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void fa_fwd_kernel(Params
       mvalid = mrow_ok && word < p.W;
     }
   };
-  auto mask_store_queued = [&](u32* mb) __attribute__((always_inline)) {
-    if (MODE == kBitmask) {
-      mb[m_row * NKB + m_word] = mq_valid ? mq : 0u;
-      mq = mreg;
-      mq_valid = mvalid;
-    }
+  auto mask_store = [&](u32* mb) __attribute__((always_inline)) {
+    if (MODE == kBitmask) mb[m_row * NKB + m_word] = mvalid ? mreg : 0u;
   };
 
   // Tile class of tile j for this wave: full (no masking), skip (a 64-lane ballot finds no kept
@@ -740,9 +737,9 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void fa_fwd_kernel(Params
   // so every matrix instruction of the tile has vector work of the softmax beside it; then the
   // sum check (softmax_finish), which in the rare case redoes the tile against its row max and
   // rescales O before the next iteration adds V_j^T P_j^T.  The iteration also issues the loads
-  // of K_{j+2} and V_j (DMA into LDS) and of the mask words of tile j+3 (into a register; the
-  // words of tile j+2, loaded one iteration earlier, are stored to LDS at its end), and ends at
-  // the one workgroup barrier of the tile.  The keep words of tile j are carried in registers
+  // of K_{j+2} and V_j (DMA into LDS), waits for them, stores the mask words of tile j+2 (loaded
+  // at the end of the previous iteration) to LDS, issues the load of those of tile j+3 (into a
+  // register), and ends at the one workgroup barrier of the tile.  The keep words of tile j are carried in registers
   // from iteration j-1, so the mask buffer of tile j can be refilled during iteration j.  After
   // the last iteration one more V^T P^T product remains.  Loads past the last tile re-read the
   // last tile (in bounds, never used).
@@ -910,7 +907,7 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void fa_fwd_kernel(Params
   // Scheduling pattern of the interleaved stream, per part: each matrix instruction with the
   // operand read of a later one, a share of the tile's global loads and V^T writes (part a),
   // and VP vector instructions of the softmax (transcendentals included).
-  constexpr int NVMEM = VDMA_PER_WAVE + DMA_PER_WAVE + (MODE == kBitmask ? 1 : 0);
+  constexpr int NVMEM = VDMA_PER_WAVE + DMA_PER_WAVE;
   constexpr int VALU_A = 52 + (MODE == kBitmask ? (PAIR_MASK ? 24 : 32) : 0);  // one block: mask, P, sums
   constexpr int VALU_B = VALU_A;
 #ifndef FA_VP_ADD
@@ -964,7 +961,6 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void fa_fwd_kernel(Params
     auto issue_loads = [&]() __attribute__((always_inline)) {
       dma_tile(j2, k_fill);
       v_dma(j0, v_fill);      // V_j (packed V^T, or rows) straight into LDS
-      mask_load(tx(j + 3));   // (stays in flight past this iteration's wait)
     };
     Cls cls_nxt = classify(j1, m_nxt);
     const bool live_nxt = wave_live && j + 1 < n_tiles && !cls_nxt.skip;
@@ -1018,11 +1014,15 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void fa_fwd_kernel(Params
     softmax_finish(cls_cur, s_cur, pk);
 #pragma unroll
     for (int t = 0; t < PKS; ++t) pk_prev[t] = pk[t];
-    // This wave's K and V DMA and the mask words of tile j+2 have landed (the words of tile
-    // j+3, issued last, stay in flight).
-    constexpr int MQ = MODE == kBitmask ? 1 : 0;
-    __builtin_amdgcn_s_waitcnt(waitcnt_imm(MQ, 15));
-    mask_store_queued(m_fill);  // the words of tile j+2, loaded during the previous iteration
+    // This wave's K and V DMA and the mask words of tile j+2 (loaded at the end of the previous
+    // iteration) have landed; the words of tile j+3 go out only now, so they are the one load
+    // in flight past the barrier.
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 15));
+    mask_store(m_fill);
+    if constexpr (MODE == kBitmask) {
+      __builtin_amdgcn_sched_barrier(0);
+      mask_load(tx(j + 3));
+    }
     // This wave's LDS writes (mask words, V^T) are complete; then meet the other waves.
     __builtin_amdgcn_s_waitcnt(waitcnt_imm(63, 0));
     pipeline_barrier();
@@ -1056,7 +1056,7 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void fa_fwd_kernel(Params
     mask_load(tix(1));
     mw1 = mreg;
     mv1 = mvalid;
-    mask_load(tix(2));  // (queued: stored at the end of iteration 0)
+    mask_load(tix(2));  // (stored at the end of iteration 0)
 #pragma unroll
     for (int pass = 0; pass < QPASS; ++pass) {
       // (Buffer choices are static, so the compiler can tell these LDS accesses from the DMA
@@ -1097,8 +1097,6 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void fa_fwd_kernel(Params
     m_lds0[m_row * NKB + m_word] = mv0 ? mw0 : 0u;
     m_lds1[m_row * NKB + m_word] = mv1 ? mw1 : 0u;
   }
-  mq = mreg;
-  mq_valid = mvalid;
   __syncthreads();
   cls_cur = classify(tix(0), m_lds0);
   live_cur = wave_live && !cls_cur.skip;
