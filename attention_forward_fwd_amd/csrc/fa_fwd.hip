@@ -269,11 +269,13 @@ constexpr int waitcnt_imm(int vm, int lgkm) {
   return (vm & 15) | ((vm >> 4) << 14) | (7 << 4) | (lgkm << 8);
 }
 
-// Workgroup barrier of the tile pipeline.  The caller first waits (s_waitcnt) for exactly the
-// memory operations that other waves must see: its LDS writes and the global->LDS copies of
-// earlier iterations, while later copies stay in flight.  (__syncthreads would also wait for
-// those: its workgroup-scope fence drains every outstanding load that writes LDS.)  The empty
-// asm statements keep the compiler from moving memory accesses across the barrier.
+// Workgroup barrier of the tile pipeline.  The caller first waits (s_waitcnt) for the memory
+// operations that other waves must see: its LDS writes and all of its global->LDS copies.  A
+// vector load it issues after that wait (a register load that no other wave reads) may stay in
+// flight, which a partial wait could not express safely: the compiler is free to issue a tile's
+// loads in any order.  (__syncthreads would also drain that load: its workgroup-scope fence
+// waits for every outstanding load.)  The empty asm statements keep the compiler from moving
+// memory accesses across the barrier.
 __device__ __forceinline__ void pipeline_barrier() {
   asm volatile("" ::: "memory");
   __builtin_amdgcn_s_barrier();
