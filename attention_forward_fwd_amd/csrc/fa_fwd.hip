@@ -856,19 +856,12 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void fa_fwd_kernel(Params
       for (int e = 0; e < 4; ++e) ps_sm[e & 1] = dot2_ones<BF16>(pw[e], ps_sm[e & 1]);
     }
   };
-#ifndef FA_PAIR_MASK
-#define FA_PAIR_MASK 1
-#endif
-  constexpr bool PAIR_MASK = MODE == kBitmask && FA_PAIR_MASK;
+  constexpr bool PAIR_MASK = MODE == kBitmask;  // keep bits applied to the packed weights
   auto softmax_block = [&](const Cls& cls, f32x16 (&s)[NKB], u32x4 (&pk)[PKS], int kb32)
                            __attribute__((always_inline)) {
     if (kb32 == 0) ps_sm[0] = ps_sm[1] = 0.f;
-    if constexpr (PAIR_MASK) {
-      exp_block(s, pk, kb32, std::true_type{}, cls.wsh[kb32]);
-    } else {
-      if (MODE == kBitmask) mask_block(cls, s, kb32);
-      exp_block(s, pk, kb32, std::false_type{}, 0u);
-    }
+    if constexpr (PAIR_MASK) exp_block(s, pk, kb32, std::true_type{}, cls.wsh[kb32]);
+    else exp_block(s, pk, kb32, std::false_type{}, 0u);
   };
   auto softmax_finish = [&](const Cls& cls, f32x16 (&s)[NKB], u32x4 (&pk)[PKS]) __attribute__((always_inline)) {
     float ps = ps_sm[0] + ps_sm[1];
@@ -910,12 +903,9 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void fa_fwd_kernel(Params
   // operand read of a later one, a share of the tile's global loads and V^T writes (part a),
   // and VP vector instructions of the softmax (transcendentals included).
   constexpr int NVMEM = VDMA_PER_WAVE + DMA_PER_WAVE;
-  constexpr int VALU_A = 52 + (MODE == kBitmask ? (PAIR_MASK ? 24 : 32) : 0);  // one block: mask, P, sums
+  constexpr int VALU_A = 52 + (PAIR_MASK ? 24 : 0);  // one block: mask, P, sums
   constexpr int VALU_B = VALU_A;
-#ifndef FA_VP_ADD
-#define FA_VP_ADD 0
-#endif
-  constexpr int VPA = (VALU_A + NPV - 1) / NPV + FA_VP_ADD, VPB = (VALU_B + NQK - 1) / NQK + FA_VP_ADD;
+  constexpr int VPA = (VALU_A + NPV - 1) / NPV, VPB = (VALU_B + NQK - 1) / NQK;
   auto stream_pattern = [&](int i0, int i1, auto vp, bool with_loads, bool first)
                             __attribute__((always_inline)) {
     // (a V^T operand of the unpacked path is two reads)
@@ -971,9 +961,6 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void fa_fwd_kernel(Params
     if (MODE != kBitmask && !cls_cur.full) mask_scores(cls_cur, s_cur);
     u32x4 pk[PKS];
     u32x4 op[AH + 1];
-#ifdef FA_PRIO_A
-    __builtin_amdgcn_s_setprio(FA_PRIO_A);
-#endif
     if constexpr (KIND == 2) {
       issue_loads();
       mm_prefetch(NPV, NMM, op, k_nxt, v_prev);
@@ -994,9 +981,6 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void fa_fwd_kernel(Params
       stream_pattern(0, NPV, std::integral_constant<int, VPA>{}, true, true);
       __builtin_amdgcn_sched_barrier(0);
       // part b: S_{j+1} = K_{j+1} Q^T beside P of keys 32..63
-#ifdef FA_PRIO_B
-      __builtin_amdgcn_s_setprio(FA_PRIO_B);
-#endif
       mm_run(NPV, NMM, NMM, op, k_nxt, s_nxt, v_prev, pk_prev);
       softmax_block(cls_cur, s_cur, pk, 1);
       stream_pattern(NPV, NMM, std::integral_constant<int, VPB>{}, false, false);
@@ -1184,54 +1168,38 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void fa_fwd_kernel(Params
     return;
   }
   const float inv = lt > 0.f ? __builtin_amdgcn_rcpf(lt) : 0.f;
-#ifndef FA_OSTAGE
-#define FA_OSTAGE 1
-#endif
-  if constexpr (FA_OSTAGE) {
-    // O rows through LDS.  A lane holds 8-byte pieces of its own row, so storing from registers
-    // writes 16 bytes of each of 32 rows per instruction; instead each wave writes its rows, one
-    // half of the columns at a time (OW bytes a row, rows OW + 8 bytes apart), into a region of
-    // its own in the K buffers (no wave reads them once the key loop has ended), reads them
-    // back row-major, 16 bytes a lane, and stores whole row halves: 128-byte lines at d=128.
-    // (A wave's LDS accesses complete in order, so no barrier is needed around its region.)
-    constexpr int OW = D;               // bytes of one half of a row
-    constexpr int ORS = OW + 8;         // row stride of a region
-    constexpr int OLR = OW / 16;        // lanes per row half
-    constexpr int ORI = 64 / OLR;       // rows per store instruction
-    static_assert((NW / 2) * 32 * ORS <= T_BYTES, "O staging regions fit the K buffers");
-    if (wave_live) {
-      unsigned char* ost = (wave < NW / 2 ? k_lds0 : k_lds1) + (wave % (NW / 2)) * (32 * ORS);
+  // O rows through LDS.  A lane holds 8-byte pieces of its own row, so storing from registers
+  // writes 16 bytes of each of 32 rows per instruction; instead each wave writes its rows, one
+  // half of the columns at a time (OW bytes a row, rows OW + 8 bytes apart), into a region of
+  // its own in the K buffers (no wave reads them once the key loop has ended), reads them
+  // back row-major, 16 bytes a lane, and stores whole row halves: 128-byte lines at d=128.
+  // (A wave's LDS accesses complete in order, so no barrier is needed around its region.)
+  constexpr int OW = D;               // bytes of one half of a row
+  constexpr int ORS = OW + 8;         // row stride of a region
+  constexpr int OLR = OW / 16;        // lanes per row half
+  constexpr int ORI = 64 / OLR;       // rows per store instruction
+  static_assert((NW / 2) * 32 * ORS <= T_BYTES, "O staging regions fit the K buffers");
+  if (wave_live) {
+    unsigned char* ost = (wave < NW / 2 ? k_lds0 : k_lds1) + (wave % (NW / 2)) * (32 * ORS);
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
+    for (int h = 0; h < 2; ++h) {
 #pragma unroll
-        for (int dbl = 0; dbl < NDB / 2; ++dbl)
+      for (int dbl = 0; dbl < NDB / 2; ++dbl)
 #pragma unroll
-          for (int t4 = 0; t4 < 4; ++t4) {
-            f32x4 x;
+        for (int t4 = 0; t4 < 4; ++t4) {
+          f32x4 x;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) x[e] = oacc[h * (NDB / 2) + dbl][4 * t4 + e] * inv;
-            *(u32x2*)(ost + l32 * ORS + (32 * dbl + 8 * t4 + 4 * hl) * 2) = pack4<BF16>(x);
-          }
-#pragma unroll
-        for (int i = 0; i < 32 / ORI; ++i) {
-          const int r = lane / OLR + ORI * i, c = lane % OLR;
-          const u32x4 x = *(const u32x4*)(ost + r * ORS + 16 * c);
-          const int grow = row0 + wave * 32 + r, pos = grow / G, head = hk * G + (grow - pos * G);
-          if (pos < S) *(u32x4*)(p.o + q_batch + ((size_t)pos * Hq + head) * D + h * (D / 2) + 8 * c) = x;
+          for (int e = 0; e < 4; ++e) x[e] = oacc[h * (NDB / 2) + dbl][4 * t4 + e] * inv;
+          *(u32x2*)(ost + l32 * ORS + (32 * dbl + 8 * t4 + 4 * hl) * 2) = pack4<BF16>(x);
         }
+#pragma unroll
+      for (int i = 0; i < 32 / ORI; ++i) {
+        const int r = lane / OLR + ORI * i, c = lane % OLR;
+        const u32x4 x = *(const u32x4*)(ost + r * ORS + 16 * c);
+        const int grow = row0 + wave * 32 + r, pos = grow / G, head = hk * G + (grow - pos * G);
+        if (pos < S) *(u32x4*)(p.o + q_batch + ((size_t)pos * Hq + head) * D + h * (D / 2) + 8 * c) = x;
       }
     }
-  } else if (wave_live && my_pos < S) {
-    uint16_t* orow = p.o + q_batch + ((size_t)my_pos * Hq + my_head) * D;
-#pragma unroll
-    for (int db = 0; db < NDB; ++db)
-#pragma unroll
-      for (int t4 = 0; t4 < 4; ++t4) {
-        f32x4 x;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) x[e] = oacc[db][4 * t4 + e] * inv;
-        *(u32x2*)(orow + 32 * db + 8 * t4 + 4 * hl) = pack4<BF16>(x);
-      }
   }
   if (wave_live && my_pos < S) {
     // Log-sum-exp of the row's kept scores (natural log), from the running softmax state: the
