@@ -1197,7 +1197,9 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void fa_fwd_kernel(Params
         const int r = lane / OLR + ORI * i, c = lane % OLR;
         const u32x4 x = *(const u32x4*)(ost + r * ORS + 16 * c);
         const int grow = row0 + wave * 32 + r, pos = grow / G, head = hk * G + (grow - pos * G);
-        if (pos < S) *(u32x4*)(p.o + q_batch + ((size_t)pos * Hq + head) * D + h * (D / 2) + 8 * c) = x;
+        // (non-temporal: O is not read again here, so it need not displace K/V tiles in L2)
+        if (pos < S)
+          __builtin_nontemporal_store(x, (u32x4*)(p.o + q_batch + ((size_t)pos * Hq + head) * D + h * (D / 2) + 8 * c));
       }
     }
   }
