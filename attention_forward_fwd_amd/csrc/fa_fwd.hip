@@ -117,12 +117,16 @@ struct Params {
 constexpr int kBN = 64;           // keys per tile
 constexpr int kWide = 8;          // waves of the 256-row workgroup
 #ifndef FA_WIDE_ROWS
-#define FA_WIDE_ROWS 4096
+#define FA_WIDE_ROWS 2048
+#endif
+#ifndef FA_WIDE_ROWS_D128
+#define FA_WIDE_ROWS_D128 512
 #endif
 #ifndef FA_WIDE_ROWS_CAUSAL
 #define FA_WIDE_ROWS_CAUSAL 8192
 #endif
-constexpr int kWideRows = FA_WIDE_ROWS;   // rows per KV head (S x G) from which it is used
+constexpr int kWideRows = FA_WIDE_ROWS;   // rows per KV head (S x G) from which it is used (d=64)
+constexpr int kWideRows128 = FA_WIDE_ROWS_D128;  // (d=128: its tiles cost twice the matrix work)
 constexpr int kWideRowsCausal = FA_WIDE_ROWS_CAUSAL;   // (causal at d=64: its short tiles favour 128 rows below)
 #ifndef FA_WIDE_ROWS_CAUSAL_D128
 #define FA_WIDE_ROWS_CAUSAL_D128 4096
@@ -1412,7 +1416,7 @@ fa_status make_plan(fa_dtype dtype, fa_mask_mode mask_mode, int batch, int n_q_h
   const int n_kt = (seq_len + kBN - 1) / kBN;
   const int64_t tile_bytes = head_dim == 128 ? VtPack<128>::TILE : VtPack<64>::TILE;
   const bool pack_ok = (int64_t)n_kt * tile_bytes < ((int64_t)1 << 31);
-  const int64_t wide_rows = mask_mode != FA_MASK_CAUSAL ? kWideRows
+  const int64_t wide_rows = mask_mode != FA_MASK_CAUSAL ? (head_dim == 128 ? kWideRows128 : kWideRows)
                             : head_dim == 128 ? kWideRowsCausal128 : kWideRowsCausal;
   const int nw = rows >= wide_rows ? kWide : 4;
   const int64_t n_rt = (rows + nw * 32 - 1) / (nw * 32);

@@ -227,15 +227,23 @@ def test_plan_prefill_uses_256_row_workgroups_and_packed_v():
 
 
 def test_plan_row_thresholds():
-    # 256-row workgroups from 4096 rows per KV head (S x G), 8192 for causal at head_dim 64
+    # 256-row workgroups from these rows per KV head (S x G): 512 at head_dim 128 and 2048 at
+    # head_dim 64 (none, bitmask); causal 4096 at head_dim 128 and 8192 at head_dim 64
     assert _plan(B=8, S=4096)["rows_per_workgroup"] == 256
+    assert _plan(B=16, S=2048)["rows_per_workgroup"] == 256
+    assert _plan(B=16, S=512)["rows_per_workgroup"] == 256
+    assert _plan(B=16, S=511)["rows_per_workgroup"] == 128
+    assert _plan(B=16, S=511, mode=BITMASK)["rows_per_workgroup"] == 128
+    assert _plan(B=16, S=512, mode=BITMASK)["rows_per_workgroup"] == 256
+    assert _plan(B=16, S=2047, D=64, dtype=F16)["rows_per_workgroup"] == 128
+    assert _plan(B=16, S=2048, D=64, dtype=F16)["rows_per_workgroup"] == 256
+    assert _plan(B=16, S=1000, D=64, dtype=F16, mode=BITMASK)["rows_per_workgroup"] == 128
     assert _plan(B=8, S=4096, mode=CAUSAL)["rows_per_workgroup"] == 256
     assert _plan(B=8, S=4095, mode=CAUSAL)["rows_per_workgroup"] == 128
     assert _plan(B=2, S=4096, mode=CAUSAL, D=64, dtype=F16)["rows_per_workgroup"] == 128
     assert _plan(B=2, S=8192, mode=CAUSAL, D=64, dtype=F16)["rows_per_workgroup"] == 256
     assert _plan(B=4, S=8192, mode=CAUSAL)["rows_per_workgroup"] == 256
-    assert _plan(B=16, S=2048)["rows_per_workgroup"] == 128
-    assert _plan(B=16, S=2048, Hq=32, Hkv=8)["rows_per_workgroup"] == 256   # 2048 x 4 rows
+    assert _plan(B=16, S=256, Hq=32, Hkv=8)["rows_per_workgroup"] == 256   # 256 x 4 rows
 
 
 def test_plan_short_masked():
@@ -249,8 +257,8 @@ def test_plan_short_masked():
 
 
 @pytest.mark.parametrize("mode,rows,nw_rows,packed", [
-    (NONE, 3968, 128, 0), (NONE, 3969, 128, 1), (NONE, 4096, 256, 0), (NONE, 7936, 256, 0),
-    (NONE, 7937, 256, 1), (BITMASK, 4095, 128, 1), (BITMASK, 7937, 256, 1),
+    (NONE, 2047, 128, 0), (NONE, 2048, 256, 0), (NONE, 4096, 256, 0), (NONE, 7936, 256, 0),
+    (NONE, 7937, 256, 1), (BITMASK, 2047, 128, 0), (BITMASK, 4095, 256, 0), (BITMASK, 7937, 256, 1),
     (CAUSAL, 3968, 128, 0), (CAUSAL, 3969, 128, 1), (CAUSAL, 8191, 128, 1), (CAUSAL, 8192, 256, 1),
 ])
 def test_plan_packs_v_from_32_row_tiles(mode, rows, nw_rows, packed):

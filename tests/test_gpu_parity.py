@@ -116,7 +116,9 @@ def test_causal_few_heads_split_over_xcds(B, S, Hq, Hkv):
 
 
 @pytest.mark.parametrize("S,Hq,Hkv,mode,D,dtype", [
-    (1500, 4, 4, "none", 128, "bf16"),      # 1500 rows per KV head: 128-row tiles, V's rows
+    (400, 4, 4, "none", 128, "bf16"),       # 400 rows per KV head: 128-row tiles, V's rows
+    (1500, 4, 4, "none", 128, "bf16"),      # 1500 rows: 256-row workgroups, V's rows
+    (1500, 4, 4, "bitmask", 64, "f16"),     # 1500 rows: 128-row tiles, d64 bitmask
     (4500, 2, 2, "causal", 64, "f16"),      # 4500 rows: 128-row tiles, packed V
     (700, 8, 1, "none", 128, "bf16"),       # 5600 rows: 256-row workgroups, V's rows
     (600, 8, 1, "bitmask", 64, "f16"),      # 4800 rows: 256-row workgroups, V's rows

@@ -13,8 +13,9 @@ DEV = torch.device("cuda:0")
 
 @pytest.mark.parametrize("B,S,Hq,Hkv,D,mode,splits", [
     (1, 8192, 16, 16, 128, "none", 1),      # packed V (256-row workgroups)
-    (1, 4000, 4, 4, 64, "bitmask", 1),      # packed V (128-row workgroups, d64)
-    (1, 4096, 1, 1, 128, "causal", 0),      # automatic split-KV: packed V + partials
+    (1, 4000, 4, 4, 64, "causal", 1),       # packed V (128-row workgroups, d64)
+    (1, 8192, 2, 2, 64, "bitmask", 1),      # packed V (256-row workgroups, d64 bitmask)
+    (1, 4096, 1, 1, 128, "causal", 0),      # automatic split-KV: partials
     (1, 1100, 16, 2, 128, "none", 3),       # explicit split
 ])
 def test_caller_workspace_equals_pool(B, S, Hq, Hkv, D, mode, splits):
