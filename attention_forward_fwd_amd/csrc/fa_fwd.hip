@@ -129,7 +129,7 @@ constexpr int kWideRows = FA_WIDE_ROWS;   // rows per KV head (S x G) from which
 constexpr int kWideRows128 = FA_WIDE_ROWS_D128;  // (d=128: its tiles cost twice the matrix work)
 constexpr int kWideRowsCausal = FA_WIDE_ROWS_CAUSAL;   // (causal at d=64: its short tiles favour 128 rows below)
 #ifndef FA_WIDE_ROWS_CAUSAL_D128
-#define FA_WIDE_ROWS_CAUSAL_D128 4096
+#define FA_WIDE_ROWS_CAUSAL_D128 2048
 #endif
 constexpr int kWideRowsCausal128 = FA_WIDE_ROWS_CAUSAL_D128;  // causal at d=128
 // Row tiles per KV head from which V is packed once per call (below it, each workgroup reads V's

@@ -228,7 +228,7 @@ def test_plan_prefill_uses_256_row_workgroups_and_packed_v():
 
 def test_plan_row_thresholds():
     # 256-row workgroups from these rows per KV head (S x G): 512 at head_dim 128 and 2048 at
-    # head_dim 64 (none, bitmask); causal 4096 at head_dim 128 and 8192 at head_dim 64
+    # head_dim 64 (none, bitmask); causal 2048 at head_dim 128 and 8192 at head_dim 64
     assert _plan(B=8, S=4096)["rows_per_workgroup"] == 256
     assert _plan(B=16, S=2048)["rows_per_workgroup"] == 256
     assert _plan(B=16, S=512)["rows_per_workgroup"] == 256
@@ -239,7 +239,8 @@ def test_plan_row_thresholds():
     assert _plan(B=16, S=2048, D=64, dtype=F16)["rows_per_workgroup"] == 256
     assert _plan(B=16, S=1000, D=64, dtype=F16, mode=BITMASK)["rows_per_workgroup"] == 128
     assert _plan(B=8, S=4096, mode=CAUSAL)["rows_per_workgroup"] == 256
-    assert _plan(B=8, S=4095, mode=CAUSAL)["rows_per_workgroup"] == 128
+    assert _plan(B=8, S=2048, mode=CAUSAL)["rows_per_workgroup"] == 256
+    assert _plan(B=8, S=2047, mode=CAUSAL)["rows_per_workgroup"] == 128
     assert _plan(B=2, S=4096, mode=CAUSAL, D=64, dtype=F16)["rows_per_workgroup"] == 128
     assert _plan(B=2, S=8192, mode=CAUSAL, D=64, dtype=F16)["rows_per_workgroup"] == 256
     assert _plan(B=4, S=8192, mode=CAUSAL)["rows_per_workgroup"] == 256

@@ -272,7 +272,7 @@ def test_growing_max(mode, D, dtype, B, S, Hq, Hkv, full):
 @pytest.mark.parametrize("scale", [12.0, -12.0])
 @pytest.mark.parametrize("mode,D,dtype,B,S,Hq,Hkv,full", [
     ("none", 128, "bf16", 1, 4096, 2, 2, False),     # 256-row workgroups
-    ("causal", 128, "bf16", 1, 1100, 4, 2, True),    # 128-row workgroups
+    ("causal", 128, "bf16", 1, 1100, 4, 2, True),    # 256-row causal workgroups, V's rows
     ("bitmask", 64, "f16", 2, 700, 2, 2, True),
 ], ids=lambda x: str(x))
 def test_sharp_softmax(scale, mode, D, dtype, B, S, Hq, Hkv, full):
