@@ -138,6 +138,11 @@ constexpr int kWideRowsCausal128 = FA_WIDE_ROWS_CAUSAL_D128;  // causal at d=128
 #define FA_PACK_ROW_TILES 32
 #endif
 constexpr int kPackRowTiles = FA_PACK_ROW_TILES;
+// (causal at d=128 does half the work per row tile, so the pre-pass pays off only from 64)
+#ifndef FA_PACK_ROW_TILES_CAUSAL_D128
+#define FA_PACK_ROW_TILES_CAUSAL_D128 64
+#endif
+constexpr int kPackRowTilesCausal128 = FA_PACK_ROW_TILES_CAUSAL_D128;
 constexpr int kMaxListTiles = 2048;  // key tiles a workgroup can list from a tile summary
 constexpr int kMaxSplits = 16;       // key ranges per row tile (split-KV)
 constexpr int kNumCUs = 256;         // MI355X compute units (automatic split-KV sizing)
@@ -1443,7 +1448,8 @@ fa_status make_plan(fa_dtype dtype, fa_mask_mode mask_mode, int batch, int n_q_h
   // Packed V^T (one pre-pass over V) when kPackRowTiles or more row-tile workgroups would
   // otherwise each transpose a KV head's V in their operand reads.
   pl->nw = nw;
-  pl->vpack = pack_ok && n_rt >= kPackRowTiles;
+  pl->vpack = pack_ok && n_rt >= (mask_mode == FA_MASK_CAUSAL && head_dim == 128 ? kPackRowTilesCausal128
+                                                                                : kPackRowTiles);
   pl->n_split = n_split;
   pl->n_kt = n_kt;
   pl->n_rb = n_rb;

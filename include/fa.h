@@ -38,8 +38,9 @@
  * aligned (mask: 4-byte aligned).  o must not alias q, k, v or mask.  The call never
  * synchronises; its work is enqueued on `stream` (a hipStream_t; NULL = default stream):
  *   - when a KV head's rows (seq_len x n_q_heads / n_kv_heads) make 32 or more row tiles of the
- *     call's workgroups (fa_fwd_plan's packed_v: causal at head_dim 64 from 3969 rows, every
- *     other case from 7937 rows), two kernels: a
+ *     call's workgroups, 64 for causal at head_dim 128 (fa_fwd_plan's packed_v: causal at
+ *     head_dim 64 from 3969 rows, causal at head_dim 128 from 16129 rows, every other case from
+ *     7937 rows), two kernels: a
  *     pre-pass that packs V into transposed tiles in a temporary device buffer (batch x
  *     n_kv_heads x ceil(seq_len / 64) x 64 x head_dim x 2 bytes, about the size of V), then the
  *     attention kernel.  The buffer is allocated and freed stream-ordered on `stream`

@@ -270,6 +270,14 @@ def test_plan_packs_v_from_32_row_tiles(mode, rows, nw_rows, packed):
     assert (p["workspace_bytes"] > 0) == bool(packed) and p["kernels"] == 1 + packed
 
 
+def test_plan_causal_d128_packs_v_from_64_row_tiles():
+    # causal at head_dim 128 does half the work per row tile: V is packed from 64 row tiles
+    for rows, packed in ((8192, 0), (16128, 0), (16129, 1)):
+        p = _plan(mode=CAUSAL, B=1, Hq=1, Hkv=1, S=rows)
+        assert p["rows_per_workgroup"] == 256 and p["packed_v"] == packed, (rows, p)
+    assert _plan(mode=NONE, B=1, Hq=1, Hkv=1, S=8192)["packed_v"] == 1
+
+
 def test_plan_split_kv():
     # explicit shares are capped at the key tiles; the partials are n x B x S x Hq x (d + 2) x 4 B
     p = _plan(B=1, Hq=1, Hkv=1, S=130, splits=16)

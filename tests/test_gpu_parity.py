@@ -245,7 +245,7 @@ def test_no_out_of_bounds_writes(S):
 # row sum run repeatedly, on every workgroup shape.
 @pytest.mark.parametrize("mode,D,dtype,B,S,Hq,Hkv,full", [
     ("none", 128, "bf16", 1, 4096, 2, 2, False),     # 256-row workgroups, V's rows
-    ("causal", 128, "bf16", 1, 8192, 1, 1, False),   # 256-row causal workgroups, packed V^T
+    ("causal", 128, "bf16", 1, 16384, 1, 1, False),  # 256-row causal workgroups, packed V^T
     ("none", 128, "bf16", 1, 1024, 8, 2, True),      # GQA group of 4, 256-row workgroups
     ("causal", 128, "bf16", 2, 700, 4, 4, True),     # 128-row workgroups, V's rows
     ("bitmask", 64, "f16", 2, 1000, 2, 2, True),     # 128-row workgroups, V's rows

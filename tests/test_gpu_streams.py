@@ -22,8 +22,9 @@ def _inputs(B, S, Hq, Hkv, D, dtype, mode, seed):
 
 @pytest.mark.parametrize("mode", ["none", "causal", "bitmask"])
 def test_side_stream_matches_default_stream(mode):
-    # 8192 positions x 2 heads: 32 or 64 row tiles per KV head, so V is packed by the pre-pass
-    # into a workspace from the pool; split-KV takes its partials from the same pool.
+    # 8192 positions x 2 heads: 32 row tiles per KV head, so V is packed by the pre-pass into a
+    # workspace from the pool (not for causal, which packs from 64); split-KV takes its partials
+    # from the same pool.
     w, q, k, v, m = _inputs(1, 8192, 2, 2, 128, "bf16", mode, seed=21000)
     log(f"case side stream {mode}")
     o_ref = fa_fwd(q, k, v, mode=mode, scale=w.scale, mask=m)

@@ -23,7 +23,7 @@ def _case(B, S, Hq, Hkv, D, mode, seed):
 
 @pytest.mark.parametrize("first,second,splits", [
     ((1, 8192, 16, 16, 128, "none"), (1, 8192, 4, 4, 128, "none"), 1),         # packed V^T
-    ((1, 8192, 16, 2, 128, "causal"), (1, 3000, 8, 2, 128, "causal"), 1),      # GQA, causal
+    ((1, 8192, 16, 2, 128, "causal"), (1, 6000, 8, 2, 128, "causal"), 1),      # GQA, causal
     ((1, 8192, 4, 4, 64, "bitmask"), (1, 8000, 2, 2, 64, "bitmask"), 1),      # d64 masked, packed V^T
     ((1, 8192, 1, 1, 128, "none"), (1, 4096, 1, 1, 128, "none"), 0),           # auto split-KV
     ((1, 2000, 4, 4, 128, "bitmask"), (1, 1500, 2, 2, 128, "bitmask"), 4),     # explicit split
