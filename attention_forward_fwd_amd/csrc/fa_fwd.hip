@@ -1463,12 +1463,19 @@ fa_status make_plan(fa_dtype dtype, fa_mask_mode mask_mode, int batch, int n_q_h
   return FA_OK;
 }
 
+// Measurement hook (fa_set_kernel_events): HIP events to record around the attention kernel of
+// this thread's next call.
+thread_local hipEvent_t t_kernel_events[2] = {nullptr, nullptr};
+
 // fa_fwd, fa_fwd_lse and fa_fwd_ex: validation first (no HIP call), then the launches.
 fa_status run_fwd(fa_dtype dtype, fa_mask_mode mask_mode, int batch, int n_q_heads,
                   int n_kv_heads, int seq_len, int head_dim, float scale, const void* q,
                   const void* k, const void* v, const uint32_t* mask, const uint32_t* tiles,
                   int kv_splits, void* o, float* lse, void* user_ws, uint64_t user_ws_bytes,
                   bool use_static_scratch, void* stream) {
+  // (the hook's events serve this call only, whatever its outcome)
+  const hipEvent_t ev_start = t_kernel_events[0], ev_stop = t_kernel_events[1];
+  t_kernel_events[0] = t_kernel_events[1] = nullptr;
   if (!q || !k || !v || !o) {
     // (an unknown dtype or mode is reported first, as the plan would)
     if (dtype != FA_DTYPE_F16 && dtype != FA_DTYPE_BF16) return FA_ERR_UNSUPPORTED;
@@ -1553,6 +1560,7 @@ fa_status run_fwd(fa_dtype dtype, fa_mask_mode mask_mode, int batch, int n_q_hea
     e = head_dim == 128 ? launch_pack<128>(p, batch, s) : launch_pack<64>(p, batch, s);
   }
   const bool bf16 = dtype == FA_DTYPE_BF16;
+  if (e == hipSuccess && ev_start) e = hipEventRecord(ev_start, s);
   if (e == hipSuccess) {
     if (bf16)
       e = head_dim == 128 ? launch_mode<true, 128>(mask_mode, p, vpack, nw, s)
@@ -1561,6 +1569,7 @@ fa_status run_fwd(fa_dtype dtype, fa_mask_mode mask_mode, int batch, int n_q_hea
       e = head_dim == 128 ? launch_mode<false, 128>(mask_mode, p, vpack, nw, s)
                           : launch_mode<false, 64>(mask_mode, p, vpack, nw, s);
   }
+  if (e == hipSuccess && ev_stop) e = hipEventRecord(ev_stop, s);
   if (e == hipSuccess && n_split > 1) {
     if (bf16)
       e = head_dim == 128 ? launch_merge<true, 128>(p, lse, s) : launch_merge<true, 64>(p, lse, s);
@@ -1577,6 +1586,13 @@ fa_status run_fwd(fa_dtype dtype, fa_mask_mode mask_mode, int batch, int n_q_hea
 }  // namespace
 
 extern "C" {
+
+fa_status fa_set_kernel_events(void* start, void* stop) {
+  if ((start == nullptr) != (stop == nullptr)) return FA_ERR_NULL_PTR;
+  t_kernel_events[0] = (hipEvent_t)start;
+  t_kernel_events[1] = (hipEvent_t)stop;
+  return FA_OK;
+}
 
 fa_status fa_fwd(fa_dtype dtype, fa_mask_mode mask_mode, int batch, int n_q_heads,
                  int n_kv_heads, int seq_len, int head_dim, float scale, const void* q,

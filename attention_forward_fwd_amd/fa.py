@@ -22,7 +22,7 @@ STATUS = {0: "FA_OK", 1: "FA_ERR_NULL_PTR", 2: "FA_ERR_BAD_SHAPE", 3: "FA_ERR_UN
           4: "FA_ERR_BAD_MASK_MODE", 5: "FA_ERR_HIP", 6: "FA_ERR_BAD_SCALE", 7: "FA_ERR_WORKSPACE",
           8: "FA_ERR_SCRATCH_LIMIT"}
 EXPORTS = ("fa_fwd", "fa_fwd_lse", "fa_fwd_ex", "fa_fwd_noalloc", "fa_fwd_plan", "fa_pack_mask",
-           "fa_mask_tiles", "fa_status_string", "fa_abi_version")
+           "fa_mask_tiles", "fa_status_string", "fa_abi_version", "fa_set_kernel_events")
 
 _lib = None
 
@@ -97,12 +97,32 @@ def load() -> ctypes.CDLL:
         lib.fa_status_string.argtypes = [ctypes.c_int]
         lib.fa_abi_version.restype = ctypes.c_int
         lib.fa_abi_version.argtypes = []
+        lib.fa_set_kernel_events.restype = ctypes.c_int
+        lib.fa_set_kernel_events.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
         _lib = lib
     return _lib
 
 
 def fa_status_string(status: int) -> str:
     return load().fa_status_string(int(status)).decode()
+
+
+def set_kernel_events(start=None, stop=None) -> None:
+    """Measurement hook (fa_set_kernel_events): the next call made on this thread records the
+    torch.cuda.Events `start` and `stop` (already recorded once, so that they exist) on its
+    stream around its attention kernel; start.elapsed_time(stop) is then that kernel's duration.
+    (None, None) clears the hook."""
+    if (start is None) != (stop is None):
+        raise ValueError("give both events or neither")
+    handles = []
+    for ev in (start, stop):
+        h = 0 if ev is None else int(ev.cuda_event)
+        if ev is not None and h == 0:
+            raise ValueError("record each event once before passing it (torch creates it then)")
+        handles.append(h)
+    st = load().fa_set_kernel_events(handles[0] or None, handles[1] or None)
+    if st != 0:
+        raise FaError(st, fa_status_string(st))
 
 
 def fa_fwd_raw(dtype: int, mask_mode: int, batch: int, n_q_heads: int, n_kv_heads: int,

@@ -48,8 +48,8 @@
  *     use on each device and keeps until the process ends (memory freed to it is retained);
  *   - otherwise the attention kernel alone.
  * A caller that must not allocate passes its own buffer to fa_fwd_ex (`workspace`, sized by
- * fa_fwd_plan) and no pool is used.  The library keeps no other state.  Calls are safe from
- * several host threads.
+ * fa_fwd_plan) and no pool is used.  The library keeps no other state (besides the per-thread
+ * event pair of fa_set_kernel_events).  Calls are safe from several host threads.
  *
  * Errors: arguments are validated first, synchronously, with no HIP call; on error nothing is
  * enqueued and o is untouched.  A failed workspace allocation or a launch error reported by
@@ -67,7 +67,7 @@
 extern "C" {
 #endif
 
-#define FA_ABI_VERSION 8
+#define FA_ABI_VERSION 9
 
 typedef enum {
   FA_MASK_NONE = 0,     /* every key kept */
@@ -231,6 +231,18 @@ const char* fa_status_string(fa_status status);
 
 /* FA_ABI_VERSION of the loaded library. */
 int fa_abi_version(void);
+
+/* Measurement hook, for timing the attention kernel apart from the V pre-pass and the split-KV
+ * merge (a roofline divides a kernel's own work by its own duration).  `start` and `stop` are
+ * hipEvent_t handles, created by the caller and owned by it.  The next fa_fwd, fa_fwd_lse,
+ * fa_fwd_ex or fa_fwd_noalloc call made on the calling host thread records `start` on its stream
+ * just before the attention kernel is enqueued and `stop` just after it (after the pre-pass,
+ * before the merge); hipEventElapsedTime of the pair then gives that kernel's duration.  The
+ * pair serves that one call, whatever its outcome: a call that fails validation or fails before
+ * the attention kernel records neither, and a later call records nothing unless the hook is set
+ * again.  (NULL, NULL) clears it.  Returns FA_ERR_NULL_PTR when exactly one of the two is NULL;
+ * the recording's own HIP errors are the call's FA_ERR_HIP.  No HIP call is made here. */
+fa_status fa_set_kernel_events(void* start, void* stop);
 
 #ifdef __cplusplus
 }

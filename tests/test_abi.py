@@ -53,9 +53,9 @@ def test_no_vendor_math_library_linked():
 
 def test_abi_version_and_status_strings():
     lib = _lib()
-    assert lib.fa_abi_version() == 8
+    assert lib.fa_abi_version() == 9
     header = open(HEADER).read()
-    assert re.search(r"#define FA_ABI_VERSION 8\b", header)
+    assert re.search(r"#define FA_ABI_VERSION 9\b", header)
     # the first five failure codes in the boundary's order; extensions after them
     for name, code in (("FA_OK", 0), ("FA_ERR_NULL_PTR", 1), ("FA_ERR_BAD_SHAPE", 2),
                        ("FA_ERR_UNSUPPORTED", 3), ("FA_ERR_BAD_MASK_MODE", 4), ("FA_ERR_HIP", 5),
@@ -68,6 +68,21 @@ def test_abi_version_and_status_strings():
         s = fa.fa_status_string(code)
         assert s and isinstance(s, str)
     assert fa.fa_status_string(12345) == "unknown status"
+
+
+def test_kernel_events_hook_arguments():
+    # Setting or clearing the hook makes no HIP call; exactly one NULL event is refused.  A pair
+    # set before a call that fails validation is consumed by that call (it records nothing: the
+    # fake handles below are never passed to HIP).
+    lib = _lib()
+    assert lib.fa_set_kernel_events(None, None) == 0
+    assert lib.fa_set_kernel_events(0x1000, None) == 1
+    assert lib.fa_set_kernel_events(None, 0x1000) == 1
+    assert lib.fa_set_kernel_events(0x1000, 0x2000) == 0
+    assert fa.fa_fwd_raw(1, 0, 1, 1, 1, 64, 128, 1.0, 0, 0x10000, 0x10000, 0, 0x10000, 0) == 1
+    assert lib.fa_set_kernel_events(None, None) == 0
+    with pytest.raises(ValueError):
+        fa.set_kernel_events(object(), None)
 
 
 # Arguments that must be rejected synchronously, before any HIP call (no GPU is touched, so
