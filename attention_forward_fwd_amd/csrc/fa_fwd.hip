@@ -822,9 +822,10 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void fa_fwd_kernel(Params
   // 16ks + 8 + 4hl + 0..3, the key order of a V^T unit), and summed per lane from the rounded
   // values (v_dot2 against (1, 1)), so numerator and denominator see the same P.  The weights
   // are >= 0, so a lane's sum bounds each of its weights: when no lane's sum exceeds kSumBound
-  // (the common case) the tile is done with alpha = 1 and no row max at all.  Otherwise -- the
-  // first live tile of a row (m still at its -1e30 floor makes the weights infinite), or scores
-  // that rose far above m -- the wave recomputes the tile (softmax_finish): the row max, m_new,
+  // (the common case) the tile is done with alpha = 1 and no row max at all.  Otherwise -- a
+  // row's first kept key past its first tile (m still at its -1e30 floor, set from the first
+  // tile's row max before the loop, makes the weights infinite), or scores that rose far above
+  // m -- the wave recomputes the tile (softmax_finish): the row max, m_new,
   // alpha = 2^(m_old - m_new), P and the sums.  Every weight therefore stays below kSumBound
   // (finite in fp16, far from overflow in the fp32 sums), and O / l and the LSE are the same
   // function of (m, l) whatever m is.  An all -inf tile gives P = 0 and leaves m and l alone.
@@ -872,25 +873,29 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void fa_fwd_kernel(Params
     if constexpr (PAIR_MASK) exp_block(s, pk, kb32, std::true_type{}, cls.wsh[kb32]);
     else exp_block(s, pk, kb32, std::false_type{}, 0u);
   };
+  // Row max of a tile's (masked) scores: two in-lane chains of 3-input maxima (v_max3_f32), one
+  // per 32-key block, then across the two lane halves.
+  auto row_max = [&](const f32x16 (&s)[NKB]) __attribute__((always_inline)) {
+    float mx2[NKB];
+#pragma unroll
+    for (int kb32 = 0; kb32 < NKB; ++kb32) {
+      const f32x16& v = s[kb32];
+      float m = __builtin_fmaxf(__builtin_fmaxf(v[0], v[1]), v[2]);
+#pragma unroll
+      for (int e = 3; e < 15; e += 2) m = __builtin_fmaxf(__builtin_fmaxf(m, v[e]), v[e + 1]);
+      mx2[kb32] = __builtin_fmaxf(m, v[15]);
+    }
+    static_assert(NKB == 2, "two 32-key blocks per tile");
+    return max_halves(__builtin_fmaxf(mx2[0], mx2[1]));
+  };
   auto softmax_finish = [&](const Cls& cls, f32x16 (&s)[NKB], u32x4 (&pk)[PKS]) __attribute__((always_inline)) {
     float ps = ps_sm[0] + ps_sm[1];
     float alpha = 1.f;
     if (__builtin_amdgcn_ballot_w64(!(ps <= kSumBound))) {  // (a NaN or infinite sum included)
       // (the weights were masked after the exp: mask the scores themselves for the row max)
       if constexpr (PAIR_MASK) mask_scores(cls, s);
-      // Row max: two in-lane chains of 3-input maxima (v_max3_f32), one per 32-key block, then
-      // across the two lane halves; the max moves straight to the tile's max.
-      float mx2[NKB];
-#pragma unroll
-      for (int kb32 = 0; kb32 < NKB; ++kb32) {
-        const f32x16& v = s[kb32];
-        float m = __builtin_fmaxf(__builtin_fmaxf(v[0], v[1]), v[2]);
-#pragma unroll
-        for (int e = 3; e < 15; e += 2) m = __builtin_fmaxf(__builtin_fmaxf(m, v[e]), v[e + 1]);
-        mx2[kb32] = __builtin_fmaxf(m, v[15]);
-      }
-      static_assert(NKB == 2, "two 32-key blocks per tile");
-      const float mx = max_halves(__builtin_fmaxf(mx2[0], mx2[1]));
+      // The max moves straight to the tile's max.
+      const float mx = row_max(s);
       const float m_new = __builtin_fmaxf(m_run, mx * c);
       alpha = __builtin_amdgcn_exp2f(m_run - m_new);
       m_run = m_new;
@@ -1100,6 +1105,17 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void fa_fwd_kernel(Params
     u32x4 op[AH + 1];
     mm_prefetch(NPV, NMM, op, k_lds0, v_lds1);
     mm_run(NPV, NMM, NMM, op, k_lds0, sA, v_lds1, pk_prev);
+#ifndef FA_M0
+#define FA_M0 1
+#endif
+    if (FA_M0) {
+      // The running max starts at the first tile's row max (its masked scores), so that tile
+      // passes the sum check instead of being computed twice: the same m the check's redo
+      // would set (from the -1e30 floor, alpha = 0 with O still 0), so results are unchanged.
+      // (A row whose first tile keeps no key keeps the floor.)
+      if (!cls_cur.full) mask_scores(cls_cur, sA);
+      m_run = __builtin_fmaxf(m_run, row_max(sA) * c);
+    }
   }
   __syncthreads();  // every wave has read K_0 before iteration 0 refills its buffer
   // Two loops over the walk: iterations in which every wave keeps a key in tiles j-1, j and j+1

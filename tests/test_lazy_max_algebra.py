@@ -5,7 +5,9 @@ as it stands, without the tile's row max.  A lane's partial sum of its (non-nega
 bounds each of them, so when every lane's sum of a wave (32 rows; each row's 64 keys split over
 two lane halves, keys with (key / 4) % 2 == half) stays within a bound T the tile is accepted
 with alpha = 1; otherwise the wave recomputes it with m moved to max(m, tile row max) for each
-of its rows, rescaling O and the row sum by 2^(m_old - m_new).  The normalised output and the
+of its rows, rescaling O and the row sum by 2^(m_old - m_new).  m starts at the first tile's
+row max (the kernel's start; with the -1e30 floor instead, that tile is the first redo).  The
+normalised output and the
 log-sum-exp do not depend on which m was used, as long as every change of m is rescaled.  This
 test runs that recurrence in float64 (no rounding to bf16) for several bounds and checks it
 against the oracle's plain definition: a missing rescale of O or of the row sum shows up far
@@ -27,13 +29,17 @@ def lane_sums(p):
     return np.stack([p[:, half == 0].sum(axis=1), p[:, half == 1].sum(axis=1)], axis=1)
 
 
-def online_sum_checked(q, k, v, scale, keep, bound, tile=64, wave=32):
+def online_sum_checked(q, k, v, scale, keep, bound, tile=64, wave=32, first_max=True):
     """One (batch, head): q [S, D], k/v [S, D], keep [S, S] bool.  Returns O [S, D], LSE [S], the
-    largest accepted weight and the number of recomputed (wave, tile) pairs."""
+    largest accepted weight and the number of recomputed (wave, tile) pairs.  first_max: m
+    starts at the first tile's row max of kept scores (a row with none keeps the floor)."""
     S, D = q.shape
     c = abs(scale) * LOG2E
     qs = q * np.sign(scale) if scale != 0 else q
     m = np.full(S, -1e30)
+    if first_max:
+        s0 = np.where(keep[:, :tile], (qs @ k[:tile].T) * c, -np.inf)
+        m = np.maximum(m, s0.max(axis=1))
     l = np.zeros(S)
     o = np.zeros((S, D))
     worst, redo = 0.0, 0
@@ -63,7 +69,8 @@ def online_sum_checked(q, k, v, scale, keep, bound, tile=64, wave=32):
 @pytest.mark.parametrize("bound", [1.0, 2.0 ** 15, 2.0 ** 60])
 @pytest.mark.parametrize("mode", ["none", "causal", "bitmask"])
 @pytest.mark.parametrize("grow", [False, True])
-def test_sum_checked_online_softmax_equals_definition(bound, mode, grow):
+@pytest.mark.parametrize("first_max", [True, False])
+def test_sum_checked_online_softmax_equals_definition(bound, mode, grow, first_max):
     w = inputs.Workload("lazy", "bf16", mode, 1, 300, 2, 1, 32, seed=31000 + int(np.log2(bound)) + 7 * grow)
     q, k, v = inputs.make_qkv(w)
     if grow:
@@ -77,7 +84,7 @@ def test_sum_checked_online_softmax_equals_definition(bound, mode, grow):
         words = None if mask is None else mask[0, h].numpy().view(np.uint32)
         keep = oracle.keep_rows(mode, rows, S, words)
         qq, kk, vv = (t.double().numpy()[0, :, hh, :] for t, hh in ((q, h), (k, 0), (v, 0)))
-        o, lse, worst, _ = online_sum_checked(qq, kk, vv, scale, keep, bound)
+        o, lse, worst, _ = online_sum_checked(qq, kk, vv, scale, keep, bound, first_max=first_max)
         assert worst <= bound
         np.testing.assert_allclose(o, want_o[0, :, h, :], rtol=0, atol=1e-12)
         fin = np.isfinite(want_lse[0, h])
@@ -93,7 +100,10 @@ def test_sum_check_moves_the_max_and_bounds_the_weights():
     k = inputs.growing_keys(k, 20.0)
     qq, kk, vv = (t.double().numpy()[0, :, 0, :] for t in (q, k, v))
     keep = np.ones((2048, 2048), dtype=bool)
-    _, _, worst, redo = online_sum_checked(qq, kk, vv, 1.5, keep, 2.0 ** 15)
+    _, _, worst, redo_floor = online_sum_checked(qq, kk, vv, 1.5, keep, 2.0 ** 15, first_max=False)
+    _, _, worst_first, redo = online_sum_checked(qq, kk, vv, 1.5, keep, 2.0 ** 15)
     n_waves = 2048 // 32
-    assert worst <= 2.0 ** 15
-    assert redo >= 3 * n_waves     # the first tile of every wave, and more as the keys grow
+    assert worst <= 2.0 ** 15 and worst_first <= 2.0 ** 15
+    assert redo_floor >= 3 * n_waves  # the first tile of every wave, and more as the keys grow
+    # starting from the first tile's max saves exactly that first redo of every wave
+    assert redo == redo_floor - n_waves
