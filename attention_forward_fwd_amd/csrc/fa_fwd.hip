@@ -1105,17 +1105,12 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void fa_fwd_kernel(Params
     u32x4 op[AH + 1];
     mm_prefetch(NPV, NMM, op, k_lds0, v_lds1);
     mm_run(NPV, NMM, NMM, op, k_lds0, sA, v_lds1, pk_prev);
-#ifndef FA_M0
-#define FA_M0 1
-#endif
-    if (FA_M0) {
-      // The running max starts at the first tile's row max (its masked scores), so that tile
-      // passes the sum check instead of being computed twice: the same m the check's redo
-      // would set (from the -1e30 floor, alpha = 0 with O still 0), so results are unchanged.
-      // (A row whose first tile keeps no key keeps the floor.)
-      if (!cls_cur.full) mask_scores(cls_cur, sA);
-      m_run = __builtin_fmaxf(m_run, row_max(sA) * c);
-    }
+    // The running max starts at the first tile's row max (its masked scores), so that tile
+    // passes the sum check instead of being computed twice: the same m the check's redo would
+    // set (from the -1e30 floor, alpha = 0 with O still 0), so results are unchanged.  (A row
+    // whose first tile keeps no key keeps the floor.)
+    if (!cls_cur.full) mask_scores(cls_cur, sA);
+    m_run = __builtin_fmaxf(m_run, row_max(sA) * c);
   }
   __syncthreads();  // every wave has read K_0 before iteration 0 refills its buffer
   // Two loops over the walk: iterations in which every wave keeps a key in tiles j-1, j and j+1
