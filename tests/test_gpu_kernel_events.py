@@ -56,3 +56,26 @@ def test_kernel_events_bracket_the_attention_kernel(S, H, splits, what):
     fa_fwd(q, k, v, scale=w.scale, kv_splits=splits)
     torch.cuda.synchronize()
     assert abs(a.elapsed_time(kb) - t_end) < 1e-3
+
+
+@pytest.mark.parametrize("entry", ["fa_fwd_lse", "fa_fwd_noalloc"])
+def test_kernel_events_other_entry_points(entry):
+    # The other entry points record the pair the same way (packed V: the pre-pass stays outside).
+    from attention_forward_fwd_amd import fa_fwd_lse, fa_fwd_noalloc
+    w = inputs.Workload("events", "bf16", "causal", 1, 16384, 1, 1, 128, seed=23500)
+    q, k, v = (t.to(DEV) for t in inputs.make_qkv(w))
+    log(f"case kernel events via {entry}")
+    o_ref = fa_fwd(q, k, v, mode="causal", scale=w.scale)
+    out = torch.empty_like(q)
+    call = {"fa_fwd_lse": lambda: fa_fwd_lse(q, k, v, mode="causal", scale=w.scale, out=out),
+            "fa_fwd_noalloc": lambda: fa_fwd_noalloc(q, k, v, out, mode="causal", scale=w.scale)}[entry]
+    ka, kb, a, b = _events(4)
+    a.record()
+    set_kernel_events(ka, kb)
+    call()
+    b.record()
+    torch.cuda.synchronize()
+    t_kernel, t_call = ka.elapsed_time(kb), a.elapsed_time(b)
+    log(f"  kernel {t_kernel * 1e3:.1f} us, call {t_call * 1e3:.1f} us")
+    assert torch.equal(out, o_ref)
+    assert 0.0 < t_kernel < t_call
