@@ -11,7 +11,7 @@ import pytest
 import torch
 
 from attention_forward_fwd_amd import inputs
-from gpu_util import check_full, check_sampled, log, run_gpu, to64, compare
+from gpu_util import check_full, check_sampled, log, oracle_rows, run_gpu, to64, compare
 import oracle
 
 pytestmark = pytest.mark.gpu
@@ -264,6 +264,34 @@ def test_growing_max(mode, D, dtype, B, S, Hq, Hkv, full):
         check_full(q, k, v, mode, w.scale, m, label)
     else:
         check_sampled(q, k, v, mode, w.scale, m, label, seed=w.seed)
+
+
+# The running max starts at the first tile's row max.  Rows that keep no key in their first
+# 64-key tile start from the -1e30 floor and take the redo on their first live tile; rows that
+# keep keys only in the first tile never move it; the rest keep a random half.  With growing
+# keys the max keeps moving after the first tile too.  The split-KV case starts every key range
+# from its own first tile.
+@pytest.mark.parametrize("D,dtype,B,S,Hq,Hkv,splits", [
+    (128, "bf16", 1, 1000, 4, 2, 1),   # 256-row workgroups
+    (64, "f16", 2, 700, 2, 2, 1),      # 128-row workgroups
+    (128, "bf16", 1, 1500, 2, 1, 3),   # split-KV key ranges
+], ids=lambda x: str(x))
+def test_first_tile_without_kept_keys(D, dtype, B, S, Hq, Hkv, splits):
+    from attention_forward_fwd_amd import fa_fwd
+    w = inputs.Workload("first", dtype, "bitmask", B, S, Hq, Hkv, D, seed=18000 + S + D)
+    q, k, v = inputs.make_qkv(w)
+    k = inputs.growing_keys(k, 20.0)
+    m = inputs.make_bitmask(w).clone()
+    rows = torch.arange(S)
+    m[:, :, rows[rows % 4 == 0], :2] = 0     # nothing kept in the first tile
+    m[:, :, rows[rows % 4 == 1], 2:] = 0     # kept keys only in the first tile
+    label = f"first tile without kept keys d{D} {dtype} B{B} S{S} H{Hq}/{Hkv} splits={splits}"
+    log(f"case {label}")
+    dev = torch.device("cuda:0")
+    o = fa_fwd(q.to(dev), k.to(dev), v.to(dev), mode="bitmask", scale=w.scale, mask=m.to(dev),
+               kv_splits=splits)
+    want = oracle_rows(q, k, v, "bitmask", w.scale, m)
+    compare(to64(o), want, q.dtype, label)
 
 
 # Sharp softmax: scaled scores spread over hundreds of exp2 units, so a row's maximum jumps far
