@@ -121,3 +121,22 @@ def test_lse_every_element_written():
     x = lse.cpu()
     assert not torch.isnan(x).any(), "an LSE element was not written"
     assert torch.isneginf(x[0, :, 5]).all()
+
+
+@pytest.mark.parametrize("D,dtype", [(128, "bf16"), (64, "f16")])
+def test_lse_first_tile_without_kept_keys(D, dtype):
+    # Rows that keep no key in their first tile (the running max starts at its floor and moves
+    # at the first live tile) beside rows that keep keys only there, with growing keys; plus
+    # rows with no kept key at all (-inf).
+    S, Hq, Hkv = 700, 4, 2
+    w = inputs.Workload("first", dtype, "bitmask", 1, S, Hq, Hkv, D, seed=18500 + D)
+    q, k, v = inputs.make_qkv(w)
+    k = inputs.growing_keys(k, 20.0)
+    m = inputs.make_bitmask(w).clone()
+    rows = torch.arange(S)
+    m[:, :, rows[rows % 4 == 0], :2] = 0
+    m[:, :, rows[rows % 4 == 1], 2:] = 0
+    m = inputs.empty_rows(m, [3, 350])
+    label = f"lse first tile without kept keys d={D} {dtype}"
+    log(f"case {label}")
+    check_full_lse(q, k, v, "bitmask", w.scale, m, label)
