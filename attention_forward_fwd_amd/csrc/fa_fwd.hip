@@ -42,18 +42,21 @@
 //     key rows past it read as zeros and are masked, so their probabilities are exactly 0.  Q is
 //     staged once through LDS into registers.
 //   * Softmax: exp2 with log2(e) folded into the scale, running max floored at -1e30 so a
-//     fully masked row never makes NaN, masked scores set to -inf with one bit-field extract
-//     and one bit-field insert.  The running max is lazy and checked after the fact: a tile's
-//     weights are formed against the max as it stands, and only when some lane's sum of them
-//     exceeds 2^15 (which bounds every weight) does the wave take the tile's row max and redo
-//     the tile, rescaling O and the row sum (every lane multiplies: no per-lane branch).  With
-//     it the common tile needs no row max and no rescale.
+//     fully masked row never makes NaN.  Causal and ragged tiles set masked scores to -inf (one
+//     bit-field extract and one 3-input bit operation per score); with a bit mask the keep bits
+//     clear the packed weights after the exp (1.5 instructions per key).  The running max
+//     starts at the first tile's row max and is lazy, checked after the fact: a tile's weights
+//     are formed against the max as it stands, and only when some lane's sum of them exceeds
+//     2^15 (which bounds every weight) does the wave take the tile's row max and redo the tile,
+//     rescaling O and the row sum (every lane multiplies: no per-lane branch).  With it the
+//     common tile needs no row max and no rescale.
 //   * Skips: per wave and tile, the keep bits of the wave's rows are voted with a 64-lane
 //     ballot.  A skipped tile's weights are exactly 0.  Causal workgroups stop at their last
 //     live tile, and on the diagonal tail (and in the walk over a mask summary) a wave whose
 //     tiles j-1 and j+1 are both dead skips the iteration's matrix work.
 //   * Scheduling: workgroups are remapped so each of the 8 XCDs gets a contiguous range of
-//     tiles (tiles of one KV head share that XCD's L2); causal row tiles run longest first.
+//     tiles (tiles of one KV head share that XCD's L2); causal row tiles run longest first,
+//     ordered so each XCD's four shader engines get equal work.
 //   * Optional outputs and schedules (fa_fwd_ex): each row's log-sum-exp from the running
 //     softmax state; in bitmask mode a walk over only the key tiles a per-block mask summary
 //     marks live (no loads for the others); split-KV, where shares of a row tile's key range
@@ -800,8 +803,10 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void fa_fwd_kernel(Params
     }
   };
 
-  // Masked scores -> -inf (bit-field extract of the keep bit + bit-field insert), for tiles
-  // that are not full.  A tile with all-zero keep words becomes all -inf, whatever s held.
+  // Masked scores -> -inf (a bit-field extract of the keep bit, then one 3-input bit operation
+  // that selects s or -inf), for tiles that are not full (with a bit mask: only for a row max,
+  // in the prologue and the redo).  A tile with all-zero keep words becomes all -inf, whatever
+  // s held.
   auto mask_block = [&](const Cls& cls, f32x16 (&s)[NKB], int kb32) __attribute__((always_inline)) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
